@@ -1,0 +1,160 @@
+/*
+ * tri_attn.h -- C ABI of the MI355X (gfx950) TriangleMix prefill-attention
+ * library (libtriattn.so).
+ *
+ * What is computed.  One attention layer of a long-context prefill, as the
+ * TriangleMix pages describe it (blog post "TriangleMix", sections "介绍" and
+ * "速度"; 36kr interview with Yang Yuqing, technical-motivation paragraphs):
+ * shallow layers keep dense causal attention, deep layers use the static
+ * "triangle" pattern, which keeps the streaming region (the leading sink keys
+ * plus a sliding window along the diagonal) and the final "Last Q-K" rows, and
+ * skips the middle Q-K region, so its cost grows as O(N) instead of O(N^2).
+ *
+ * For batch b, query head h, query row i (g = h / (heads_q / heads_kv)):
+ *   K_i   = { j <= i : j < sink  or  i - j < window  or  i >= N - last_q }
+ *           (triangle), or { j <= i } (causal);
+ *   z_ij  = softmax_scale * <q[b,h,i,:], k[b,g,j,:]>
+ *   o[b,h,i,:] = sum_{j in K_i} softmax_j(z_i.) * v[b,g,j,:]
+ *   lse[b,h,i] = ln sum_{j in K_i} exp(z_ij)        (natural log)
+ *
+ * Conventions.
+ *   - Every call returns TRI_OK (0) or a negative tri_status; nothing throws
+ *     across the ABI.  On error, tri_attn_last_error() returns a message.
+ *   - All argument validation happens before any HIP runtime call, so every
+ *     error path can be exercised on a machine without a GPU.
+ *   - The library never allocates, frees or copies device memory and keeps no
+ *     global state other than the per-thread error message.  The caller owns
+ *     every buffer, host or device.
+ *   - Device calls enqueue on the caller's stream and return; results are
+ *     bit-deterministic for identical inputs (fixed traversal order, no
+ *     atomics).  Device faults surface at the caller's next synchronisation.
+ */
+#ifndef TRI_ATTN_H
+#define TRI_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TRI_OK = 0,
+  TRI_ERR_INVALID = -1,     /* malformed argument (null, negative, inconsistent) */
+  TRI_ERR_CAPACITY = -2,    /* output arrays too small; *nnz_out holds the need   */
+  TRI_ERR_UNSUPPORTED = -3, /* valid but not implemented (head_dim, tile size)   */
+  TRI_ERR_HIP = -4          /* the HIP runtime reported an error at launch        */
+} tri_status;
+
+typedef enum { TRI_MASK_TRIANGLE = 0, TRI_MASK_CAUSAL = 1 } tri_mask_kind;
+typedef enum { TRI_DTYPE_BF16 = 0, TRI_DTYPE_F32 = 1 } tri_dtype;
+enum { TRI_TILE_FULL = 0, TRI_TILE_PARTIAL = 1 };
+
+/* Tile shape the GPU kernel walks (query rows x key columns per tile). */
+enum { TRI_KERNEL_BLOCK_Q = 128, TRI_KERNEL_BLOCK_K = 64 };
+
+/* Static mask of one layer.  sink, window and last_q are token counts; values
+ * larger than seqlen are legal and mean "the whole range".  window >= 1, so
+ * the diagonal is always kept and no row is ever empty. */
+typedef struct {
+  int64_t seqlen;   /* N >= 0 (N == 0: nothing to do)                        */
+  int32_t block_q;  /* planner: any >= 1; prefill: TRI_KERNEL_BLOCK_Q        */
+  int32_t block_k;  /* planner: any >= 1; prefill: TRI_KERNEL_BLOCK_K        */
+  int32_t kind;     /* tri_mask_kind                                         */
+  int32_t reserved; /* must be 0                                             */
+  int64_t sink;     /* >= 0: keys j < sink are kept by every row             */
+  int64_t window;   /* >= 1: keys with i - j < window are kept               */
+  int64_t last_q;   /* >= 0: rows i >= N - last_q keep every key j <= i      */
+} tri_mask_params;
+
+/*
+ * tri_attn_plan -- host-only tile planner (pure, deterministic, no HIP call).
+ *
+ * Lists, for every query tile t (rows [t*block_q, min(N,(t+1)*block_q))), the
+ * key tiles kt (columns [kt*block_k, (kt+1)*block_k)) that hold at least one
+ * kept (row, column) pair, in ascending kt, as CSR:
+ *   row_ptr[t] .. row_ptr[t+1]-1 index k_tile[] and flags[];
+ *   flags[e] = TRI_TILE_FULL when every valid row of the query tile keeps every
+ *   column of the key tile (columns >= N never count as kept), else
+ *   TRI_TILE_PARTIAL.
+ * The kernel computes kept tiles only, masking inside PARTIAL ones; this is the
+ * index-driven tile skipping the FlashPrefill page (section 2.3) contrasts with
+ * branch-per-block skipping.
+ *
+ * Sizing call: row_ptr, k_tile and flags all NULL -> writes *n_qtiles_out and
+ * *nnz_out only.  Fill call: all three non-NULL; row_ptr has n_qtiles + 1
+ * entries, k_tile and flags have `capacity` entries.  If capacity < nnz the call
+ * writes *n_qtiles_out and *nnz_out and returns TRI_ERR_CAPACITY.
+ * n_qtiles_out and nnz_out must be non-NULL.
+ */
+int tri_attn_plan(const tri_mask_params* mp, int32_t* row_ptr, int32_t* k_tile,
+                  uint8_t* flags, int64_t capacity, int32_t* n_qtiles_out,
+                  int64_t* nnz_out);
+
+/* Device tensors of one layer.  Strides are in elements, for the (batch, head,
+ * token) axes; the channel axis is contiguous.  q, k, v are bf16, 16-byte
+ * aligned, with token strides that are multiples of 8 elements.  o is bf16
+ * (8-byte aligned, token stride a multiple of 4) or f32 (16-byte aligned,
+ * token stride a multiple of 4).  lse (f32) may be NULL. */
+typedef struct {
+  const void* q;       /* [B, Hq,  N, d] */
+  const void* k;       /* [B, Hkv, N, d] */
+  const void* v;       /* [B, Hkv, N, d] */
+  void* o;             /* [B, Hq,  N, d] in o_dtype */
+  float* lse;          /* [B, Hq,  N] natural-log log-sum-exp, or NULL */
+  int32_t batch;       /* >= 1 */
+  int32_t heads_q;     /* >= 1, multiple of heads_kv */
+  int32_t heads_kv;    /* >= 1; query head h reads KV head h / (heads_q/heads_kv) */
+  int32_t head_dim;    /* 64 or 128 */
+  int64_t seqlen;      /* N; must equal mp->seqlen in tri_attn_prefill */
+  int64_t q_stride[3];
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+  int64_t lse_stride[2];
+  float softmax_scale; /* finite, > 0 (1/sqrt(head_dim) for standard attention) */
+  int32_t o_dtype;     /* tri_dtype */
+} tri_attn_tensors;
+
+/*
+ * tri_attn_prefill -- triangle (or any planned) layer on the GPU.
+ *
+ * d_row_ptr, d_k_tile, d_flags are device copies of tri_attn_plan's output for
+ * the same *mp (block_q = TRI_KERNEL_BLOCK_Q, block_k = TRI_KERNEL_BLOCK_K); the
+ * caller owns them and keeps them alive until the work completes.  `stream` is
+ * a hipStream_t (NULL = the null stream).  Returns after enqueueing.
+ */
+int tri_attn_prefill(const tri_attn_tensors* t, const tri_mask_params* mp,
+                     const int32_t* d_row_ptr, const int32_t* d_k_tile,
+                     const uint8_t* d_flags, void* stream);
+
+/*
+ * dense_causal_prefill -- dense (shallow) layer: the same kernel walking the
+ * full causal tile list, enumerated in the kernel (equal to tri_attn_plan with
+ * kind = TRI_MASK_CAUSAL and the kernel tile shape).
+ */
+int dense_causal_prefill(const tri_attn_tensors* t, void* stream);
+
+/* Message for the last non-OK return on this thread ("" if none). */
+const char* tri_attn_last_error(void);
+
+/* ABI version of this header (incremented on incompatible change). */
+int tri_attn_abi_version(void);
+
+/*
+ * tri_attn_work_item -- host-only view of the kernel's block schedule, for
+ * testing that the launch covers every (batch, head, query tile) exactly once.
+ * For launch block index `bid` of a launch over (batch, heads_q, heads_kv,
+ * seqlen, kind, last_q), writes the work item it computes (or -1 in all three
+ * when that block has none) and the grid size to *grid_out.
+ */
+int tri_attn_work_item(int32_t batch, int32_t heads_q, int32_t heads_kv,
+                       int64_t seqlen, int32_t kind, int64_t last_q, int64_t bid,
+                       int32_t* b_out, int32_t* h_out, int32_t* qtile_out,
+                       int64_t* grid_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRI_ATTN_H */

@@ -1,0 +1,123 @@
+"""TriangleMix triangle-attention prefill for MI355X (gfx950).
+
+Thin Python layer over libtriattn.so (C ABI in include/tri_attn.h).  PyTorch
+supplies device memory and the stream; the tile planner and the attention
+kernel run in the library.  There is no fallback path: if the library is not
+built, importing the binding raises.
+
+    from static_triangle_sparse_amd import prefill
+    o, lse = prefill(q, k, v, mode="triangle", sink=128, window=2048, last_q=128)
+
+q: [B, Hq, N, d] bf16 CUDA tensor, k/v: [B, Hkv, N, d] (any strides with the
+channel axis contiguous).  Returns o [B, Hq, N, d] (bf16 or f32) and the
+natural-log LSE [B, Hq, N] (f32).
+"""
+from __future__ import annotations
+
+import math
+
+from ._abi import (  # noqa: F401
+    TRI_DTYPE_BF16, TRI_DTYPE_F32, TRI_ERR_CAPACITY, TRI_ERR_HIP, TRI_ERR_INVALID,
+    TRI_ERR_UNSUPPORTED, TRI_KERNEL_BLOCK_K, TRI_KERNEL_BLOCK_Q, TRI_MASK_CAUSAL,
+    TRI_MASK_TRIANGLE, TRI_OK, TRI_TILE_FULL, TRI_TILE_PARTIAL, AttnTensors, MaskParams,
+    TriAttnError, dense_causal_prefill, last_error, load, mask_params, tri_attn_abi_version,
+    tri_attn_plan, tri_attn_prefill, tri_attn_work_item,
+)
+
+__all__ = [
+    "prefill", "DevicePlan", "device_plan", "make_tensors", "tri_attn_plan", "tri_attn_prefill",
+    "dense_causal_prefill", "mask_params", "TriAttnError", "last_error", "layer_mode",
+]
+
+
+def layer_mode(layer: int, tri_start: int) -> str:
+    """TriangleMix layer policy: layers before ``tri_start`` stay dense causal,
+    the rest use the triangle pattern (TriangleMix blog, "性能": 12 dense layers
+    suffice for the Llama-3 models, 20 for Qwen2.5)."""
+    return "causal" if layer < tri_start else "triangle"
+
+
+class DevicePlan:
+    """Host plan (numpy) plus its device copy (torch int32/uint8 tensors)."""
+
+    def __init__(self, mp: MaskParams, device):
+        import torch
+        self.mp = mp
+        self.row_ptr, self.k_tile, self.flags = tri_attn_plan(mp)
+        self.d_row_ptr = torch.from_numpy(self.row_ptr).to(device)
+        # never hand the kernel an empty allocation
+        n = max(1, self.k_tile.size)
+        self.d_k_tile = torch.zeros(n, dtype=torch.int32, device=device)
+        self.d_flags = torch.zeros(n, dtype=torch.uint8, device=device)
+        if self.k_tile.size:
+            self.d_k_tile.copy_(torch.from_numpy(self.k_tile))
+            self.d_flags.copy_(torch.from_numpy(self.flags))
+
+    @property
+    def nnz(self) -> int:
+        return int(self.k_tile.size)
+
+
+_PLAN_CACHE = {}
+
+
+def device_plan(seqlen, kind="triangle", sink=0, window=1, last_q=0, device="cuda") -> DevicePlan:
+    mp = mask_params(seqlen, kind, sink, window, last_q)
+    key = (mp.seqlen, mp.kind, mp.sink, mp.window, mp.last_q, str(device))
+    p = _PLAN_CACHE.get(key)
+    if p is None:
+        p = DevicePlan(mp, device)
+        _PLAN_CACHE[key] = p
+    return p
+
+
+def make_tensors(q, k, v, o, lse=None, scale=None) -> AttnTensors:
+    """Descriptor of torch tensors q, k, v [B,H,N,d] (bf16), o (bf16/f32), lse (f32)."""
+    import torch
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        if x.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16")
+        if x.dim() != 4 or x.stride(3) != 1:
+            raise ValueError(f"{name} must be 4-D [B, H, N, d] with a contiguous last axis")
+    if o.dtype not in (torch.bfloat16, torch.float32) or o.stride(3) != 1:
+        raise ValueError("o must be bf16 or f32 with a contiguous last axis")
+    B, Hq, N, d = q.shape
+    t = AttnTensors()
+    t.q, t.k, t.v, t.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
+    t.lse = lse.data_ptr() if lse is not None else None
+    t.batch, t.heads_q, t.heads_kv, t.head_dim = B, Hq, k.shape[1], d
+    t.seqlen = N
+    for field, x in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", o)):
+        getattr(t, field)[:] = [x.stride(0), x.stride(1), x.stride(2)]
+    if lse is not None:
+        if lse.dtype != torch.float32 or lse.stride(2) != 1:
+            raise ValueError("lse must be f32 [B, Hq, N] with a contiguous last axis")
+        t.lse_stride[:] = [lse.stride(0), lse.stride(1)]
+    t.softmax_scale = (1.0 / math.sqrt(d)) if scale is None else float(scale)
+    t.o_dtype = TRI_DTYPE_BF16 if o.dtype == torch.bfloat16 else TRI_DTYPE_F32
+    return t
+
+
+def prefill(q, k, v, mode="triangle", sink=0, window=1, last_q=0, o_dtype=None, scale=None,
+            out=None, lse=None, stream=None):
+    """One attention layer on the GPU; returns (o, lse).  ``mode`` is
+    "triangle" (planned tile list) or "causal" (dense layer)."""
+    import torch
+    B, Hq, N, d = q.shape
+    if o_dtype is None:
+        o_dtype = torch.bfloat16
+    if out is None:
+        out = torch.empty((B, Hq, N, d), dtype=o_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    t = make_tensors(q, k, v, out, lse, scale)
+    s = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
+    if mode == "causal":
+        dense_causal_prefill(t, s)
+    elif mode == "triangle":
+        p = device_plan(N, "triangle", sink, window, last_q, q.device)
+        tri_attn_prefill(t, p.mp, p.d_row_ptr.data_ptr(), p.d_k_tile.data_ptr(),
+                         p.d_flags.data_ptr(), s)
+    else:
+        raise ValueError(f"unknown mode {mode!r}")
+    return out, lse

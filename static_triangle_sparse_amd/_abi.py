@@ -1,0 +1,176 @@
+"""ctypes binding of libtriattn.so (include/tri_attn.h).
+
+Argument marshalling only: every step of the attention path runs in the
+library (host planner, gfx950 kernel).  The structures below mirror the C
+header field by field.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtriattn.so")
+
+TRI_OK = 0
+TRI_ERR_INVALID = -1
+TRI_ERR_CAPACITY = -2
+TRI_ERR_UNSUPPORTED = -3
+TRI_ERR_HIP = -4
+
+TRI_MASK_TRIANGLE = 0
+TRI_MASK_CAUSAL = 1
+TRI_DTYPE_BF16 = 0
+TRI_DTYPE_F32 = 1
+TRI_TILE_FULL = 0
+TRI_TILE_PARTIAL = 1
+TRI_KERNEL_BLOCK_Q = 128
+TRI_KERNEL_BLOCK_K = 64
+
+_STATUS_NAMES = {
+    TRI_OK: "TRI_OK", TRI_ERR_INVALID: "TRI_ERR_INVALID", TRI_ERR_CAPACITY: "TRI_ERR_CAPACITY",
+    TRI_ERR_UNSUPPORTED: "TRI_ERR_UNSUPPORTED", TRI_ERR_HIP: "TRI_ERR_HIP",
+}
+
+
+class TriAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class MaskParams(ctypes.Structure):
+    _fields_ = [
+        ("seqlen", ctypes.c_int64),
+        ("block_q", ctypes.c_int32),
+        ("block_k", ctypes.c_int32),
+        ("kind", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("sink", ctypes.c_int64),
+        ("window", ctypes.c_int64),
+        ("last_q", ctypes.c_int64),
+    ]
+
+
+class AttnTensors(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+        ("batch", ctypes.c_int32),
+        ("heads_q", ctypes.c_int32),
+        ("heads_kv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("seqlen", ctypes.c_int64),
+        ("q_stride", ctypes.c_int64 * 3),
+        ("k_stride", ctypes.c_int64 * 3),
+        ("v_stride", ctypes.c_int64 * 3),
+        ("o_stride", ctypes.c_int64 * 3),
+        ("lse_stride", ctypes.c_int64 * 2),
+        ("softmax_scale", ctypes.c_float),
+        ("o_dtype", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the in-tree library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m static_triangle_sparse_amd.build` "
+            "(there is no fallback path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    lib.tri_attn_plan.argtypes = [P(MaskParams), P(ctypes.c_int32), P(ctypes.c_int32),
+                                  P(ctypes.c_uint8), ctypes.c_int64, P(ctypes.c_int32),
+                                  P(ctypes.c_int64)]
+    lib.tri_attn_plan.restype = ctypes.c_int
+    lib.tri_attn_prefill.argtypes = [P(AttnTensors), P(MaskParams), ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.tri_attn_prefill.restype = ctypes.c_int
+    lib.dense_causal_prefill.argtypes = [P(AttnTensors), ctypes.c_void_p]
+    lib.dense_causal_prefill.restype = ctypes.c_int
+    lib.tri_attn_last_error.argtypes = []
+    lib.tri_attn_last_error.restype = ctypes.c_char_p
+    lib.tri_attn_abi_version.argtypes = []
+    lib.tri_attn_abi_version.restype = ctypes.c_int
+    lib.tri_attn_work_item.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int64, ctypes.c_int32, ctypes.c_int64,
+                                       ctypes.c_int64, P(ctypes.c_int32), P(ctypes.c_int32),
+                                       P(ctypes.c_int32), P(ctypes.c_int64)]
+    lib.tri_attn_work_item.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().tri_attn_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != TRI_OK:
+        raise TriAttnError(status, last_error())
+
+
+def mask_params(seqlen, kind=TRI_MASK_TRIANGLE, sink=0, window=1, last_q=0,
+                block_q=TRI_KERNEL_BLOCK_Q, block_k=TRI_KERNEL_BLOCK_K) -> MaskParams:
+    if isinstance(kind, str):
+        kind = {"triangle": TRI_MASK_TRIANGLE, "causal": TRI_MASK_CAUSAL}[kind]
+    return MaskParams(int(seqlen), int(block_q), int(block_k), int(kind), 0, int(sink),
+                      int(window), int(last_q))
+
+
+def tri_attn_plan(mp: MaskParams):
+    """Host tile planner.  Returns (row_ptr int32[nq+1], k_tile int32[nnz],
+    flags uint8[nnz]) as numpy arrays."""
+    lib = load()
+    nq = ctypes.c_int32()
+    nnz = ctypes.c_int64()
+    _check(lib.tri_attn_plan(ctypes.byref(mp), None, None, None, 0, ctypes.byref(nq),
+                             ctypes.byref(nnz)))
+    row_ptr = np.zeros(nq.value + 1, dtype=np.int32)
+    k_tile = np.zeros(max(1, nnz.value), dtype=np.int32)
+    flags = np.zeros(max(1, nnz.value), dtype=np.uint8)
+    _check(lib.tri_attn_plan(
+        ctypes.byref(mp), row_ptr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+        k_tile.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+        flags.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), nnz.value, ctypes.byref(nq),
+        ctypes.byref(nnz)))
+    return row_ptr, k_tile[:nnz.value], flags[:nnz.value]
+
+
+def tri_attn_prefill(t: AttnTensors, mp: MaskParams, d_row_ptr: int, d_k_tile: int,
+                     d_flags: int, stream: int) -> None:
+    """Enqueue a planned (triangle) layer; pointers are device addresses."""
+    _check(load().tri_attn_prefill(ctypes.byref(t), ctypes.byref(mp), d_row_ptr, d_k_tile,
+                                   d_flags, stream))
+
+
+def dense_causal_prefill(t: AttnTensors, stream: int) -> None:
+    """Enqueue a dense causal layer."""
+    _check(load().dense_causal_prefill(ctypes.byref(t), stream))
+
+
+def tri_attn_abi_version() -> int:
+    return load().tri_attn_abi_version()
+
+
+def tri_attn_work_item(batch, heads_q, heads_kv, seqlen, kind, last_q, bid):
+    """(b, h, qtile, grid) of launch block ``bid`` (qtile -1: idle block)."""
+    b = ctypes.c_int32()
+    h = ctypes.c_int32()
+    t = ctypes.c_int32()
+    grid = ctypes.c_int64()
+    _check(load().tri_attn_work_item(batch, heads_q, heads_kv, seqlen, kind, last_q, bid,
+                                     ctypes.byref(b), ctypes.byref(h), ctypes.byref(t),
+                                     ctypes.byref(grid)))
+    return b.value, h.value, t.value, grid.value

@@ -1,0 +1,182 @@
+// C ABI of libtriattn: argument validation, error reporting and dispatch to
+// the gfx950 kernel.  Every check runs before the first HIP runtime call, so
+// each error path can be driven from a host without a GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "tri_attn.h"
+#include "tri_attn_internal.h"
+
+namespace triattn {
+
+namespace {
+thread_local char g_error[512] = "";
+}
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_error, sizeof(g_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void clear_error() { g_error[0] = '\0'; }
+
+namespace {
+
+constexpr int64_t kMaxSeqlen = int64_t(1) << 30;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_strides(const char* name, const int64_t* s, int n) {
+  for (int i = 0; i < n; ++i)
+    if (s[i] < 0) return fail(TRI_ERR_INVALID, "%s stride %d is negative", name, i);
+  return TRI_OK;
+}
+
+int validate_tensors(const tri_attn_tensors* t) {
+  if (!t) return fail(TRI_ERR_INVALID, "tensor descriptor pointer is NULL");
+  if (!t->q || !t->k || !t->v || !t->o)
+    return fail(TRI_ERR_INVALID, "q, k, v and o must be non-NULL device pointers");
+  if (t->batch < 1 || t->heads_q < 1 || t->heads_kv < 1)
+    return fail(TRI_ERR_INVALID, "batch, heads_q and heads_kv must be >= 1");
+  if (t->heads_q % t->heads_kv != 0)
+    return fail(TRI_ERR_INVALID, "heads_q (%d) must be a multiple of heads_kv (%d)", t->heads_q,
+                t->heads_kv);
+  if (t->head_dim != 64 && t->head_dim != 128)
+    return fail(TRI_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", t->head_dim);
+  if (t->seqlen < 0) return fail(TRI_ERR_INVALID, "seqlen must be >= 0");
+  if (t->seqlen >= kMaxSeqlen) return fail(TRI_ERR_UNSUPPORTED, "seqlen must be < 2^30");
+  if (t->o_dtype != TRI_DTYPE_BF16 && t->o_dtype != TRI_DTYPE_F32)
+    return fail(TRI_ERR_INVALID, "o_dtype must be TRI_DTYPE_BF16 or TRI_DTYPE_F32");
+  if (!(t->softmax_scale > 0.0f) || !isfinite(t->softmax_scale))
+    return fail(TRI_ERR_INVALID, "softmax_scale must be finite and > 0");
+  int st;
+  if ((st = check_strides("q", t->q_stride, 3)) != TRI_OK) return st;
+  if ((st = check_strides("k", t->k_stride, 3)) != TRI_OK) return st;
+  if ((st = check_strides("v", t->v_stride, 3)) != TRI_OK) return st;
+  if ((st = check_strides("o", t->o_stride, 3)) != TRI_OK) return st;
+  if (t->lse && (st = check_strides("lse", t->lse_stride, 2)) != TRI_OK) return st;
+  if (!aligned(t->q, 16) || !aligned(t->k, 16) || !aligned(t->v, 16))
+    return fail(TRI_ERR_INVALID, "q, k and v must be 16-byte aligned");
+  for (int i = 0; i < 3; ++i) {
+    if (t->q_stride[i] % 8 || t->k_stride[i] % 8 || t->v_stride[i] % 8)
+      return fail(TRI_ERR_INVALID, "q/k/v strides must be multiples of 8 elements (16 bytes)");
+    if (t->o_stride[i] % 4)
+      return fail(TRI_ERR_INVALID, "o strides must be multiples of 4 elements");
+  }
+  if (!aligned(t->o, t->o_dtype == TRI_DTYPE_BF16 ? 8 : 16))
+    return fail(TRI_ERR_INVALID, "o must be %d-byte aligned", t->o_dtype == TRI_DTYPE_BF16 ? 8 : 16);
+  if (t->lse && !aligned(t->lse, 4)) return fail(TRI_ERR_INVALID, "lse must be 4-byte aligned");
+  const int64_t nq = (t->seqlen + TRI_KERNEL_BLOCK_Q - 1) / TRI_KERNEL_BLOCK_Q;
+  const int64_t blocks = static_cast<int64_t>(t->batch) * t->heads_q * (nq + kNumXcd);
+  if (blocks >= INT32_MAX) return fail(TRI_ERR_UNSUPPORTED, "launch grid exceeds 2^31-1 blocks");
+  return TRI_OK;
+}
+
+AttnLaunch make_launch(const tri_attn_tensors* t, bool causal, int64_t sink, int64_t window,
+                       int64_t last_q) {
+  AttnLaunch a{};
+  a.q = t->q;
+  a.k = t->k;
+  a.v = t->v;
+  a.o = t->o;
+  a.lse = t->lse;
+  memcpy(a.q_stride, t->q_stride, sizeof(a.q_stride));
+  memcpy(a.k_stride, t->k_stride, sizeof(a.k_stride));
+  memcpy(a.v_stride, t->v_stride, sizeof(a.v_stride));
+  memcpy(a.o_stride, t->o_stride, sizeof(a.o_stride));
+  if (t->lse) memcpy(a.lse_stride, t->lse_stride, sizeof(a.lse_stride));
+  a.head_dim = t->head_dim;
+  a.o_bf16 = t->o_dtype == TRI_DTYPE_BF16 ? 1 : 0;
+  a.causal = causal ? 1 : 0;
+  const int64_t N = t->seqlen;
+  a.seqlen = static_cast<int32_t>(N);
+  // Values past N mean "everything": j < N, i - j <= N - 1 and i >= 0 always.
+  a.sink = static_cast<int32_t>(std::min(sink, N));
+  a.window = static_cast<int32_t>(std::max<int64_t>(1, std::min(window, N)));
+  a.last_q = static_cast<int32_t>(std::min(last_q, N));
+  a.scale = t->softmax_scale;
+  a.sched = make_schedule(t->batch, t->heads_q, t->heads_kv, N, TRI_KERNEL_BLOCK_Q, causal,
+                          causal ? N : a.last_q);
+  return a;
+}
+
+}  // namespace
+}  // namespace triattn
+
+using namespace triattn;
+
+extern "C" const char* tri_attn_last_error(void) { return g_error; }
+
+extern "C" int tri_attn_abi_version(void) { return 1; }
+
+extern "C" int tri_attn_prefill(const tri_attn_tensors* t, const tri_mask_params* mp,
+                                const int32_t* d_row_ptr, const int32_t* d_k_tile,
+                                const uint8_t* d_flags, void* stream) {
+  clear_error();
+  int st = validate_mask(mp);
+  if (st != TRI_OK) return st;
+  if ((st = validate_tensors(t)) != TRI_OK) return st;
+  if (mp->block_q != TRI_KERNEL_BLOCK_Q || mp->block_k != TRI_KERNEL_BLOCK_K)
+    return fail(TRI_ERR_UNSUPPORTED, "the kernel walks %dx%d tiles; plan has %dx%d",
+                TRI_KERNEL_BLOCK_Q, TRI_KERNEL_BLOCK_K, mp->block_q, mp->block_k);
+  if (mp->seqlen != t->seqlen)
+    return fail(TRI_ERR_INVALID, "mask seqlen %lld differs from tensor seqlen %lld",
+                static_cast<long long>(mp->seqlen), static_cast<long long>(t->seqlen));
+  if (!d_row_ptr || !d_k_tile || !d_flags)
+    return fail(TRI_ERR_INVALID, "plan arrays (row_ptr, k_tile, flags) must be non-NULL");
+  if (!aligned(d_row_ptr, 4) || !aligned(d_k_tile, 4))
+    return fail(TRI_ERR_INVALID, "row_ptr and k_tile must be 4-byte aligned");
+  if (t->seqlen == 0) return TRI_OK;
+  AttnLaunch a = make_launch(t, mp->kind == TRI_MASK_CAUSAL, mp->sink, mp->window, mp->last_q);
+  a.causal = 0;  // walk the caller's list even for a causal plan
+  a.row_ptr = d_row_ptr;
+  a.k_tile = d_k_tile;
+  a.flags = d_flags;
+  if (mp->kind == TRI_MASK_CAUSAL) {
+    // a causal plan masks like the causal kernel: make the triangle predicate
+    // keep every j <= i
+    a.last_q = a.seqlen;
+  }
+  return launch_attn_fwd(a, stream);
+}
+
+extern "C" int dense_causal_prefill(const tri_attn_tensors* t, void* stream) {
+  clear_error();
+  int st = validate_tensors(t);
+  if (st != TRI_OK) return st;
+  if (t->seqlen == 0) return TRI_OK;
+  AttnLaunch a = make_launch(t, true, 0, 1, t->seqlen);
+  return launch_attn_fwd(a, stream);
+}
+
+extern "C" int tri_attn_work_item(int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                  int64_t seqlen, int32_t kind, int64_t last_q, int64_t bid,
+                                  int32_t* b_out, int32_t* h_out, int32_t* qtile_out,
+                                  int64_t* grid_out) {
+  clear_error();
+  if (!b_out || !h_out || !qtile_out || !grid_out)
+    return fail(TRI_ERR_INVALID, "output pointers must be non-NULL");
+  if (batch < 1 || heads_q < 1 || heads_kv < 1 || heads_q % heads_kv)
+    return fail(TRI_ERR_INVALID, "bad head counts");
+  if (seqlen < 1 || seqlen >= kMaxSeqlen) return fail(TRI_ERR_INVALID, "bad seqlen");
+  if (kind != TRI_MASK_TRIANGLE && kind != TRI_MASK_CAUSAL)
+    return fail(TRI_ERR_INVALID, "bad kind");
+  if (last_q < 0) return fail(TRI_ERR_INVALID, "last_q must be >= 0");
+  const bool causal = kind == TRI_MASK_CAUSAL;
+  const Schedule s = make_schedule(batch, heads_q, heads_kv, seqlen, TRI_KERNEL_BLOCK_Q, causal,
+                                   causal ? seqlen : std::min(last_q, seqlen));
+  const WorkItem w = schedule_item(s, bid);
+  *b_out = w.b;
+  *h_out = w.h;
+  *qtile_out = w.t;
+  *grid_out = s.grid;
+  return TRI_OK;
+}

@@ -1,0 +1,140 @@
+// Internal declarations shared by the host planner, the ABI layer and the
+// gfx950 kernel launcher of libtriattn.  Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include "tri_attn.h"
+
+namespace triattn {
+
+// Per-thread error message (tri_attn_last_error); returns `code`.
+int fail(int code, const char* fmt, ...)
+#if defined(__GNUC__)
+    __attribute__((format(printf, 2, 3)))
+#endif
+    ;
+void clear_error();
+
+int validate_mask(const tri_mask_params* mp);
+
+// ---------------------------------------------------------------- schedule
+//
+// Maps a launch block index to the (batch, query head, query tile) it
+// computes.  MI355X hands consecutive workgroups of a launch to its 8 XCDs in
+// turn (block b runs on XCD b % 8) and each XCD has its own L2, so blocks that
+// share K/V tiles (the query heads of one KV group, neighbouring query tiles)
+// are placed on the same XCD:
+//   * each (batch, KV head) group is cut into S interleaved streams of query
+//     tiles (position p goes to stream p % S), with S chosen so the number of
+//     streams is a multiple of 8; XCD x owns streams [x*spx, (x+1)*spx);
+//   * inside an XCD, blocks run position-major, then stream, then the G query
+//     heads of the group, so the blocks in flight on one XCD work on the same
+//     K/V window;
+//   * positions are ordered heaviest first: for the triangle mask the query
+//     tiles holding last-Q rows (which read every earlier key) come first in
+//     descending order, then the rest ascending; for the causal mask the
+//     tiles run in descending order.
+// Positions past the last tile of a stream leave the block idle (t = -1).
+struct Schedule {
+  int32_t batch, heads_q, heads_kv, group;  // group = heads_q / heads_kv
+  int32_t n_qtiles;                          // query tiles of 128 rows
+  int32_t causal;                            // 1: causal order, 0: triangle order
+  int32_t n_heavy;                           // triangle: tiles with last-Q rows
+  int32_t streams;                           // S: streams per KV group
+  int32_t streams_per_xcd;                   // spx
+  int32_t positions;                         // P = ceil(n_qtiles / S)
+  int64_t grid;                              // 8 * spx * P * group
+};
+
+constexpr int kNumXcd = 8;
+
+constexpr int32_t gcd_i32(int32_t a, int32_t b) {
+  while (b) {
+    const int32_t r = a % b;
+    a = b;
+    b = r;
+  }
+  return a;
+}
+
+// block_q: rows per query tile; last_q: clamped to [0, N].
+constexpr Schedule make_schedule(int32_t batch, int32_t heads_q, int32_t heads_kv, int64_t N,
+                                 int32_t block_q, bool causal, int64_t last_q) {
+  Schedule s{};
+  s.batch = batch;
+  s.heads_q = heads_q;
+  s.heads_kv = heads_kv;
+  s.group = heads_q / heads_kv;
+  s.n_qtiles = static_cast<int32_t>((N + block_q - 1) / block_q);
+  s.causal = causal ? 1 : 0;
+  if (causal || last_q <= 0) {
+    s.n_heavy = causal ? s.n_qtiles : 0;
+  } else {
+    const int64_t first_heavy = (N - last_q) / block_q;  // tile of row N - last_q
+    s.n_heavy = static_cast<int32_t>(s.n_qtiles - first_heavy);
+  }
+  const int32_t n_groups = batch * heads_kv;
+  s.streams = kNumXcd / gcd_i32(n_groups, kNumXcd);
+  s.streams_per_xcd = n_groups * s.streams / kNumXcd;
+  s.positions = (s.n_qtiles + s.streams - 1) / s.streams;
+  s.grid = static_cast<int64_t>(kNumXcd) * s.streams_per_xcd * s.positions * s.group;
+  return s;
+}
+
+struct WorkItem {
+  int32_t b, h, t;  // t = -1: idle block
+};
+
+constexpr WorkItem schedule_item(const Schedule& s, int64_t bid) {
+  const int64_t x = bid % kNumXcd;
+  const int64_t u = bid / kNumXcd;
+  const int64_t per_pos = static_cast<int64_t>(s.streams_per_xcd) * s.group;
+  const int64_t pi = u / per_pos;
+  const int64_t rem = u % per_pos;
+  const int64_t si = rem / s.group;
+  const int32_t hh = static_cast<int32_t>(rem % s.group);
+  const int64_t stream = x * s.streams_per_xcd + si;
+  const int32_t grp = static_cast<int32_t>(stream / s.streams);
+  const int64_t p = pi * s.streams + stream % s.streams;
+  WorkItem w{-1, -1, -1};
+  if (bid < 0 || bid >= s.grid || p >= s.n_qtiles) return w;
+  int32_t t = -1;
+  if (s.causal) {
+    t = s.n_qtiles - 1 - static_cast<int32_t>(p);
+  } else if (p < s.n_heavy) {
+    t = s.n_qtiles - 1 - static_cast<int32_t>(p);
+  } else {
+    t = static_cast<int32_t>(p) - s.n_heavy;
+  }
+  w.b = grp / s.heads_kv;
+  w.h = (grp % s.heads_kv) * s.group + hh;
+  w.t = t;
+  return w;
+}
+
+// ---------------------------------------------------------------- launch
+
+struct AttnLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3], lse_stride[2];
+  int32_t head_dim;
+  int32_t o_bf16;  // 1: bf16 output, 0: f32 output
+  int32_t causal;  // 1: in-kernel causal tile range, 0: explicit tile list
+  int32_t seqlen;  // N (validated < 2^30)
+  int32_t sink, window, last_q;  // clamped to [0, N] ([1, N] for window)
+  float scale;                   // softmax scale
+  const int32_t* row_ptr;
+  const int32_t* k_tile;
+  const uint8_t* flags;
+  Schedule sched;
+};
+
+// Enqueue the gfx950 kernel; returns TRI_OK or TRI_ERR_HIP.
+int launch_attn_fwd(const AttnLaunch& a, void* stream);
+
+}  // namespace triattn

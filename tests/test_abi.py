@@ -1,0 +1,191 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, validates every argument before touching HIP, and its block
+schedule covers each work item exactly once."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import static_triangle_sparse_amd as tsa
+from static_triangle_sparse_amd import _abi
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "tri_attn.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_symbols_are_exported():
+    names = _declared_functions()
+    assert {"tri_attn_plan", "tri_attn_prefill", "dense_causal_prefill",
+            "tri_attn_last_error"} <= set(names)
+    lib = ctypes.CDLL(_abi.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert tsa.tri_attn_abi_version() == 1
+
+
+# ----------------------------------------------------------- plan validation
+
+def _raw_plan(mp, row_ptr=None, k_tile=None, flags=None, capacity=0, nq=True, nnz=True):
+    lib = _abi.load()
+    nq_v = ctypes.c_int32(-7)
+    nnz_v = ctypes.c_int64(-7)
+    st = lib.tri_attn_plan(ctypes.byref(mp) if mp is not None else None, row_ptr, k_tile, flags,
+                           capacity, ctypes.byref(nq_v) if nq else None,
+                           ctypes.byref(nnz_v) if nnz else None)
+    return st, nq_v.value, nnz_v.value
+
+
+@pytest.mark.parametrize("field,value", [("seqlen", -1), ("block_q", 0), ("block_k", 0),
+                                         ("kind", 2), ("reserved", 1), ("sink", -1),
+                                         ("window", 0), ("last_q", -1)])
+def test_plan_rejects_bad_params(field, value):
+    mp = tsa.mask_params(100, "triangle", 1, 2, 3)
+    setattr(mp, field, value)
+    st, _, _ = _raw_plan(mp)
+    assert st == tsa.TRI_ERR_INVALID
+    assert tsa.last_error()
+
+
+def test_plan_null_and_capacity_errors():
+    mp = tsa.mask_params(1000, "triangle", 5, 100, 10)
+    assert _raw_plan(None)[0] == tsa.TRI_ERR_INVALID
+    assert _raw_plan(mp, nq=False)[0] == tsa.TRI_ERR_INVALID
+    assert _raw_plan(mp, nnz=False)[0] == tsa.TRI_ERR_INVALID
+    st, nq, nnz = _raw_plan(mp)
+    assert st == tsa.TRI_OK and nq == 8 and nnz > 0
+    rp = (ctypes.c_int32 * (nq + 1))()
+    kt = (ctypes.c_int32 * nnz)()
+    fl = (ctypes.c_uint8 * nnz)()
+    # partially NULL output arrays
+    assert _raw_plan(mp, rp, None, fl, nnz)[0] == tsa.TRI_ERR_INVALID
+    # too small
+    st, nq2, nnz2 = _raw_plan(mp, rp, kt, fl, nnz - 1)
+    assert st == tsa.TRI_ERR_CAPACITY and nq2 == nq and nnz2 == nnz
+    assert "capacity" in tsa.last_error()
+    assert _raw_plan(mp, rp, kt, fl, nnz)[0] == tsa.TRI_OK
+    assert tsa.last_error() == ""
+
+
+# -------------------------------------------------------- prefill validation
+
+def _good_tensors(B=1, Hq=4, Hkv=2, N=256, d=128, o_dtype=tsa.TRI_DTYPE_BF16):
+    t = tsa.AttnTensors()
+    base = 1 << 20  # fake, suitably aligned device addresses: never dereferenced
+    t.q, t.k, t.v, t.o, t.lse = base, base * 2, base * 3, base * 4, base * 5
+    t.batch, t.heads_q, t.heads_kv, t.head_dim, t.seqlen = B, Hq, Hkv, d, N
+    t.q_stride[:] = [Hq * N * d, N * d, d]
+    t.k_stride[:] = [Hkv * N * d, N * d, d]
+    t.v_stride[:] = [Hkv * N * d, N * d, d]
+    t.o_stride[:] = [Hq * N * d, N * d, d]
+    t.lse_stride[:] = [Hq * N, N]
+    t.softmax_scale = d ** -0.5
+    t.o_dtype = o_dtype
+    return t
+
+
+BAD_TENSORS = [
+    ("q", None, tsa.TRI_ERR_INVALID), ("k", None, tsa.TRI_ERR_INVALID),
+    ("v", None, tsa.TRI_ERR_INVALID), ("o", None, tsa.TRI_ERR_INVALID),
+    ("q", (1 << 20) + 8, tsa.TRI_ERR_INVALID), ("k", (1 << 21) + 2, tsa.TRI_ERR_INVALID),
+    ("o", (1 << 22) + 4, tsa.TRI_ERR_INVALID), ("lse", (1 << 22) + 2, tsa.TRI_ERR_INVALID),
+    ("batch", 0, tsa.TRI_ERR_INVALID), ("heads_q", 0, tsa.TRI_ERR_INVALID),
+    ("heads_kv", 0, tsa.TRI_ERR_INVALID), ("heads_q", 5, tsa.TRI_ERR_INVALID),
+    ("head_dim", 96, tsa.TRI_ERR_UNSUPPORTED), ("head_dim", 256, tsa.TRI_ERR_UNSUPPORTED),
+    ("seqlen", -1, tsa.TRI_ERR_INVALID), ("seqlen", 1 << 30, tsa.TRI_ERR_UNSUPPORTED),
+    ("o_dtype", 7, tsa.TRI_ERR_INVALID), ("softmax_scale", 0.0, tsa.TRI_ERR_INVALID),
+    ("softmax_scale", float("inf"), tsa.TRI_ERR_INVALID),
+    ("softmax_scale", float("nan"), tsa.TRI_ERR_INVALID),
+]
+
+
+@pytest.mark.parametrize("field,value,status", BAD_TENSORS)
+def test_dense_prefill_rejects_bad_tensors(field, value, status):
+    t = _good_tensors(o_dtype=tsa.TRI_DTYPE_F32)
+    setattr(t, field, value)
+    st = _abi.load().dense_causal_prefill(ctypes.byref(t), None)
+    assert st == status, tsa.last_error()
+    assert tsa.last_error()
+
+
+@pytest.mark.parametrize("which,idx,value", [("q_stride", 2, 100), ("k_stride", 1, 4),
+                                             ("v_stride", 0, -8), ("o_stride", 2, 2),
+                                             ("lse_stride", 0, -1)])
+def test_prefill_rejects_bad_strides(which, idx, value):
+    t = _good_tensors()
+    getattr(t, which)[idx] = value
+    assert _abi.load().dense_causal_prefill(ctypes.byref(t), None) == tsa.TRI_ERR_INVALID
+
+
+def test_triangle_prefill_rejects_bad_plan_arguments():
+    lib = _abi.load()
+    t = _good_tensors()
+    mp = tsa.mask_params(256, "triangle", 4, 64, 16)
+    P = 1 << 24
+    assert lib.tri_attn_prefill(ctypes.byref(t), None, P, P, P, None) == tsa.TRI_ERR_INVALID
+    assert lib.tri_attn_prefill(None, ctypes.byref(mp), P, P, P, None) == tsa.TRI_ERR_INVALID
+    assert lib.tri_attn_prefill(ctypes.byref(t), ctypes.byref(mp), None, P, P, None) == tsa.TRI_ERR_INVALID
+    assert lib.tri_attn_prefill(ctypes.byref(t), ctypes.byref(mp), P, None, P, None) == tsa.TRI_ERR_INVALID
+    assert lib.tri_attn_prefill(ctypes.byref(t), ctypes.byref(mp), P, P, None, None) == tsa.TRI_ERR_INVALID
+    assert lib.tri_attn_prefill(ctypes.byref(t), ctypes.byref(mp), P + 2, P, P, None) == tsa.TRI_ERR_INVALID
+    bad = tsa.mask_params(256, "triangle", 4, 64, 16, block_q=64)
+    assert lib.tri_attn_prefill(ctypes.byref(t), ctypes.byref(bad), P, P, P, None) == tsa.TRI_ERR_UNSUPPORTED
+    bad = tsa.mask_params(255, "triangle", 4, 64, 16)
+    assert lib.tri_attn_prefill(ctypes.byref(t), ctypes.byref(bad), P, P, P, None) == tsa.TRI_ERR_INVALID
+    bad = tsa.mask_params(256, "triangle", 4, 0, 16)
+    assert lib.tri_attn_prefill(ctypes.byref(t), ctypes.byref(bad), P, P, P, None) == tsa.TRI_ERR_INVALID
+
+
+def test_empty_sequence_is_a_no_op():
+    # N == 0 validates and returns before any HIP call
+    t = _good_tensors(N=0)
+    assert _abi.load().dense_causal_prefill(ctypes.byref(t), None) == tsa.TRI_OK
+    mp = tsa.mask_params(0, "triangle", 4, 64, 16)
+    P = 1 << 24
+    assert _abi.load().tri_attn_prefill(ctypes.byref(t), ctypes.byref(mp), P, P, P, None) == tsa.TRI_OK
+
+
+# ----------------------------------------------------------------- schedule
+
+def _cover(B, Hq, Hkv, N, kind, last_q):
+    _, _, _, grid = tsa.tri_attn_work_item(B, Hq, Hkv, N, kind, last_q, 0)
+    seen = {}
+    order = []
+    for bid in range(grid):
+        b, h, t, _ = tsa.tri_attn_work_item(B, Hq, Hkv, N, kind, last_q, bid)
+        if t < 0:
+            continue
+        assert (b, h, t) not in seen, (b, h, t)
+        seen[(b, h, t)] = bid
+        order.append((bid, b, h, t))
+    nq = -(-N // 128)
+    assert set(seen) == {(b, h, t) for b in range(B) for h in range(Hq) for t in range(nq)}
+    assert grid <= B * Hq * (nq + 8)
+    return seen, order
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N", [(1, 1, 1, 512), (1, 32, 8, 4096), (1, 28, 4, 3000),
+                                        (2, 6, 3, 1000), (3, 7, 7, 129), (1, 4, 1, 1),
+                                        (4, 32, 8, 640), (1, 12, 12, 9000)])
+@pytest.mark.parametrize("kind", [tsa.TRI_MASK_TRIANGLE, tsa.TRI_MASK_CAUSAL])
+def test_schedule_covers_every_item_once(B, Hq, Hkv, N, kind):
+    _cover(B, Hq, Hkv, N, kind, 128)
+
+
+def test_schedule_puts_a_kv_group_on_one_xcd_and_heavy_tiles_first():
+    # 8 KV groups: block bid runs on XCD bid % 8, which must own one group
+    seen, order = _cover(1, 32, 8, 8192, tsa.TRI_MASK_TRIANGLE, 128)
+    for (b, h, t), bid in seen.items():
+        assert bid % 8 == h // 4
+    nq = 64
+    first = [t for bid, b, h, t in order[:32]]
+    assert first == [nq - 1] * 32          # the last-Q tile of every head first
+    seen, order = _cover(1, 32, 8, 8192, tsa.TRI_MASK_CAUSAL, 0)
+    ts = [t for _, _, _, t in order]
+    assert ts == sorted(ts, reverse=True)  # causal: heaviest (longest) tiles first
