@@ -1,0 +1,321 @@
+"""Benchmark of the TriangleMix triangle-attention prefill on one MI355X.
+
+Default workload: one Llama-3-8B-shaped attention layer (32 query heads, 8 KV
+heads, head_dim 128, batch 1) at N = 131072 tokens with the triangle mask
+(sink 128, window 2048, last-Q 128), bf16 Q/K/V ~ N(0, 1) from a seeded host
+generator, bf16 O plus f32 LSE.  One step = one triangle layer (the planned
+tile list is built once, outside the timed region).  The dense causal layer
+runs on the same inputs for the triangle-vs-dense ratio.
+
+Prints one JSON line.  ``value`` is kept-tile TFLOP/s: 4 * 128 * 64 * d FLOPs
+per kept (query tile, key tile) pair per query head (partial tiles count in
+full), divided by the measured time per layer.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--config 3]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "triangle prefill ms + kept-tile TFLOP/s (% bf16 MFMA peak) at 128K, 1 GPU"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+KERNEL_SRC = os.path.join(ROOT, "static_triangle_sparse_amd", "csrc", "attn_fwd_gfx950.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_triangle_llama128k_traffic.txt")
+
+CONFIGS = {
+    1: dict(name="single head, N=512, d=64 (sink 64, window 128, last-Q 64)",
+            B=1, Hq=1, Hkv=1, N=512, d=64, sink=64, window=128, last_q=64, layers=None),
+    2: dict(name="Llama-3-8B-shaped layer (32q/8kv, d=128), N=32768",
+            B=1, Hq=32, Hkv=8, N=32768, d=128, sink=128, window=2048, last_q=128, layers=None),
+    3: dict(name="Llama-3-8B-shaped layer (32q/8kv, d=128), N=131072",
+            B=1, Hq=32, Hkv=8, N=131072, d=128, sink=128, window=2048, last_q=128, layers=None),
+    4: dict(name="Llama-3-8B-shaped 32-layer stack, N=65536, layers 0-11 dense, 12-31 triangle",
+            B=1, Hq=32, Hkv=8, N=65536, d=128, sink=128, window=2048, last_q=128,
+            layers=32, tri_start=12),
+    5: dict(name="Qwen2.5-7B-shaped 28-layer stack (28q/4kv), N=131072, layers 0-19 dense, 20-27 triangle",
+            B=1, Hq=28, Hkv=4, N=131072, d=128, sink=128, window=2048, last_q=128,
+            layers=28, tri_start=20),
+}
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(launch_flops: float):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def kept_tiles_per_head(plan) -> int:
+    return int(plan.k_tile.size)
+
+
+def causal_tiles_per_head(N: int) -> int:
+    nq = -(-N // 128)
+    return sum(min(N - 1, t * 128 + 127) // 64 + 1 for t in range(nq))
+
+
+def make_layer_inputs(cfg, seed, dev, host=True):
+    """bf16 Q, K, V on the device.  host=True: the shared seeded numpy
+    generator (bit-identical to what the parity tests use); host=False: torch's
+    device generator (stack benchmarks, where per-layer host generation of
+    tens of GB would dominate the run)."""
+    import torch
+    B, Hq, Hkv, N, d = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["N"], cfg["d"]
+    if host:
+        import synth
+        bits = synth.qkv_bf16_bits(seed, B, Hq, Hkv, N, d)
+        out = [torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16) for x in bits]
+        return out, bits
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    mk = lambda h: torch.randn((B, h, N, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    return [mk(Hq), mk(Hkv), mk(Hkv)], None
+
+
+def time_launches(fn, steps, warmup):
+    """Average ms per launch of fn() over `steps` back-to-back launches,
+    bracketed by device synchronisation; HIP events on the launch stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return start.elapsed_time(stop) / steps, wall
+
+
+def cpu_baseline(bits, cfg, plan, seconds_hint=20.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the same layer."""
+    from oracle import attention as oatt
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    N, Hq, d = cfg["N"], cfg["Hq"], cfg["d"]
+    nq = -(-N // 128)
+    rng = np.random.default_rng(1)
+    tiles = sorted({0, 1, 15, 16, 17, nq - 2, nq - 1} |
+                   (set(int(x) for x in rng.choice(np.arange(18, nq - 2), 8, replace=False))
+                    if nq > 30 else set()))
+    tiles = [t for t in tiles if 0 <= t < nq]
+    rows = np.concatenate([np.arange(t * 128, min(N, (t + 1) * 128)) for t in tiles])
+    kept = sum(int(plan.row_ptr[t + 1] - plan.row_ptr[t]) for t in tiles)
+    flops = 4.0 * 128 * 64 * d * kept * Hq * cfg["B"]
+    f64 = synth.bf16_bits_to_f64
+    q, k, v = f64(bits[0]), f64(bits[1]), f64(bits[2])
+    t0 = time.perf_counter()
+    oatt.attention(q, k, v, "triangle", cfg["sink"], cfg["window"], cfg["last_q"], rows=rows)
+    dt = time.perf_counter() - t0
+    total_flops = 4.0 * 128 * 64 * d * plan.k_tile.size * Hq * cfg["B"]
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle (OpenBLAS, {threads} threads, {cpu_model or 'cpu'}) on query "
+                   f"tiles {tiles} of all {Hq} heads ({rows.size} rows, {kept} kept tiles/head): "
+                   f"{dt:.2f} s; kept-tile FLOPs of the sample / time; full layer extrapolated "
+                   f"{dt * total_flops / flops:.1f} s"),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, choices=sorted(CONFIGS))
+    ap.add_argument("--dense-steps", type=int, default=3)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the layer shards by KV-head group with no communication; see the design notes)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import static_triangle_sparse_amd as tsa
+    dev = torch.device("cuda:0")
+    tsa.load()
+    cfg = CONFIGS[args.config]
+    print(f"[bench] config {args.config}: {cfg['name']}", file=sys.stderr, flush=True)
+
+    if cfg["layers"]:
+        return bench_stack(args, cfg, dev)
+
+    (q, k, v), bits = make_layer_inputs(cfg, 0, dev)
+    B, Hq, N, d = cfg["B"], cfg["Hq"], cfg["N"], cfg["d"]
+    o = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    plan = tsa.device_plan(N, "triangle", cfg["sink"], cfg["window"], cfg["last_q"], dev)
+    t = tsa.make_tensors(q, k, v, o, lse)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    tri = lambda: tsa.tri_attn_prefill(t, plan.mp, plan.d_row_ptr.data_ptr(),
+                                       plan.d_k_tile.data_ptr(), plan.d_flags.data_ptr(), stream)
+    dense = lambda: tsa.dense_causal_prefill(t, stream)
+
+    tri_ms, tri_wall = time_launches(tri, args.steps, args.warmup)
+    print(f"[bench] triangle: {tri_ms:.3f} ms/layer (wall {tri_wall:.3f})", file=sys.stderr, flush=True)
+    tiles = kept_tiles_per_head(plan)
+    flops = 4.0 * 128 * 64 * d * tiles * Hq * B
+    tflops = flops / (tri_ms * 1e-3) / 1e12
+
+    extra = {}
+    if not args.no_dense:
+        dense_ms, _ = time_launches(dense, args.dense_steps, 1)
+        ctiles = causal_tiles_per_head(N)
+        dflops = 4.0 * 128 * 64 * d * ctiles * Hq * B
+        extra = {"dense_ms": round(dense_ms, 4),
+                 "dense_tflops": round(dflops / (dense_ms * 1e-3) / 1e12, 2),
+                 "dense_pct_peak": round(100 * dflops / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                 "triangle_speedup_vs_dense": round(dense_ms / tri_ms, 2),
+                 "dense_kept_tiles_per_head": ctiles}
+        print(f"[bench] dense causal: {dense_ms:.3f} ms/layer", file=sys.stderr, flush=True)
+
+    if args.calib_copy_mib:
+        nbytes = args.calib_copy_mib << 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy of {args.calib_copy_mib} MiB done", file=sys.stderr, flush=True)
+        del src, dst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle sample) ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(bits, cfg, plan)
+
+    traffic = read_traffic(flops)
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(tri_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"] + " triangle prefill layer", "batch": B, "heads_q": Hq,
+                   "heads_kv": cfg["Hkv"], "head_dim": d, "seqlen": N, "sink": cfg["sink"],
+                   "window": cfg["window"], "last_q": cfg["last_q"], "tile": "128x64",
+                   "o_dtype": "bf16", "kept_tiles_per_head": tiles},
+        "triangle_ms": round(tri_ms, 4),
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        **extra,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def bench_stack(args, cfg, dev):
+    """Configs 4-5: every layer's attention back to back on one stream, layers
+    before tri_start dense causal, the rest triangle."""
+    import torch
+    import static_triangle_sparse_amd as tsa
+    B, Hq, Hkv, N, d, L = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["N"], cfg["d"], cfg["layers"]
+    layers = []
+    for l in range(L):
+        (q, k, v), _ = make_layer_inputs(cfg, 1000 + l, dev, host=False)
+        layers.append((q, k, v))
+    o = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    plan = tsa.device_plan(N, "triangle", cfg["sink"], cfg["window"], cfg["last_q"], dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    descs = [tsa.make_tensors(q, k, v, o, lse) for (q, k, v) in layers]
+    modes = [tsa.layer_mode(l, cfg["tri_start"]) for l in range(L)]
+
+    def step():
+        for t, m in zip(descs, modes):
+            if m == "causal":
+                tsa.dense_causal_prefill(t, stream)
+            else:
+                tsa.tri_attn_prefill(t, plan.mp, plan.d_row_ptr.data_ptr(), plan.d_k_tile.data_ptr(),
+                                     plan.d_flags.data_ptr(), stream)
+
+    steps = max(1, min(args.steps, 3))
+    ms, _ = time_launches(step, steps, min(args.warmup, 1))
+    tiles = kept_tiles_per_head(plan)
+    ctiles = causal_tiles_per_head(N)
+    n_dense = sum(m == "causal" for m in modes)
+    flops = 4.0 * 128 * 64 * d * Hq * B * (n_dense * ctiles + (L - n_dense) * tiles)
+    tflops = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "TriangleMix layer-stack attention ms + kept-tile TFLOP/s, 1 GPU",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "warmup": min(args.warmup, 1), "ms_per_step": round(ms, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (torch device generator, seed 1000 + layer)",
+        "config": {"workload": cfg["name"], "layers": L, "dense_layers": n_dense, "seqlen": N,
+                   "heads_q": Hq, "heads_kv": Hkv, "head_dim": d},
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

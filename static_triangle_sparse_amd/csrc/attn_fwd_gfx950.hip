@@ -4,20 +4,27 @@
 // technical motivation) and the dense causal layer use the same kernel.
 //
 // One workgroup = one (batch, query head, 128-row query tile); 4 waves, each
-// owning 32 query rows.  Per kept 64-key tile:
-//   1. K (row-major) and V (transposed to channel-major) are staged in LDS from
-//      registers that were prefetched from HBM during the previous tile;
-//   2. S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS, Q held in
+// owning 32 query rows; two workgroups share a CU.  Per kept 64-key tile:
+//   1. K and V are copied HBM -> LDS by the LDS-DMA path
+//      (global_load_lds_dwordx4: each lane's 16 bytes land at LDS base +
+//      16 * lane), double-buffered, one tile ahead of the compute, without
+//      staging registers.  Each 16-byte chunk is placed at an XOR-swizzled
+//      position in its row so that the MFMA operand reads below hit distinct
+//      LDS banks;
+//   2. S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 (K rows from LDS, Q held in
 //      registers for the whole loop).  Computing the transpose puts one query
 //      per lane, so row statistics are per-lane scalars;
 //   3. PARTIAL tiles apply the mask predicate per element, FULL tiles skip it;
-//   4. online softmax in fp32 with exp2 (log2 e folded into the scale);
+//   4. online softmax in fp32 with exp2 (log2 e folded into the scale); the
+//      accumulator is rescaled only when some row's running max grows by more
+//      than 2^8 (softmax is invariant to the reference point, and P stays below
+//      256, far inside fp32/bf16 range);
 //   5. O^T += V^T . P^T on MFMA: the fp32 scores of step 2 are already laid out
-//      as the B operand of this product once converted to bf16 (the key order
-//      of that layout is mirrored by the column order of V^T in LDS), so P never
-//      leaves registers.
-// Output O = acc / l (bf16 round-to-nearest-even or f32) and the natural-log
-// LSE = scale * m + ln l are written once per row.
+//      as the B operand of this product once converted to bf16, so P never
+//      leaves registers; the A operand V^T is read from the row-major V tile
+//      with the transposing LDS read ds_read_b64_tr_b16.
+// Output O = acc / sum(bf16 P) (stored bf16 round-to-nearest-even or f32) and
+// the natural-log LSE = scale * m + ln sum(P) are written once per row.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -28,75 +35,280 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+#define LDS_AS __attribute__((address_space(3)))
+#define GLOBAL_AS __attribute__((address_space(1)))
+
 constexpr int kBlockQ = TRI_KERNEL_BLOCK_Q;  // 128 query rows per workgroup
 constexpr int kBlockK = TRI_KERNEL_BLOCK_K;  // 64 keys per tile
 constexpr int kThreads = 256;                // 4 waves x 32 query rows
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleLog2 = 8.0f;  // rescale when a row max grows by > 2^8 in p units
 
 template <int D>
 struct Cfg {
-  static constexpr int kKStride = D * 2 + 16;      // bytes per K row in LDS (padded)
-  static constexpr int kVStride = kBlockK * 2 + 16;  // bytes per V^T row (one channel)
-  static constexpr int kKBytes = kBlockK * kKStride;
-  static constexpr int kVBytes = D * kVStride;
-  static constexpr int kBufBytes = kKBytes + kVBytes;
-  static constexpr int kQSteps = D / 16;            // k-steps of S^T = K Q^T
-  static constexpr int kOBlocks = D / 32;           // 32-channel blocks of O^T
-  static constexpr int kKLoads = kBlockK * D / 8 / kThreads;  // 16-B K chunks / thread
-  static constexpr int kVUnits = (kBlockK / 4) * (D / 8);     // 4 keys x 8 channels units
+  static constexpr int kRowBytes = D * 2;                 // one K or V row
+  static constexpr int kChunks = D / 8;                   // 16-byte chunks per row
+  static constexpr int kTileBytes = kBlockK * kRowBytes;  // one K (or V) tile
+  static constexpr int kRowsPerBlock = 1024 / kRowBytes;  // rows per 1 KiB DMA block
+  static constexpr int kDmaPerWave = kTileBytes / 1024 / 4;  // DMA instructions / wave / matrix
+  static constexpr int kQSteps = D / 16;                  // k-steps of S^T = K Q^T
+  static constexpr int kOBlocks = D / 32;                 // 32-channel blocks of O^T
 };
+
+// Swizzles (16-byte chunk c of tile row r lives at chunk c ^ swz(r)).
+// K: the S^T operand read has 32 lanes on 32 consecutive rows at one chunk;
+// V: the transposing read has each 32-lane half on 4 consecutive rows x 4
+// chunks.  Both place those reads on distinct banks.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+}
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Column (key position) of key quad `kq` (keys 4*kq..4*kq+3 of the tile) in
-// the V^T rows.  In the S^T accumulator, lane half `hi` of a 32-key block
-// holds keys {4*hi..4*hi+3, 8+4*hi..8+4*hi+3} (+16 for the next half block) in
-// registers 0..7; the PV MFMA reads those registers as k-positions
-// 8*hi..8*hi+7 of a 16-key step.  Storing key quads 1 and 2 of every 16-key
-// group swapped makes V^T's columns follow that order.
-__device__ __forceinline__ int vt_column(int kq) {
-  const int grp = kq >> 2, q = kq & 3;
-  return grp * 16 + ((q & 1) * 2 + (q >> 1)) * 4;
+// value of x in lane l ^ 32 combined with x: returns {x[l & 31], x[(l & 31) + 32]}
+__device__ __forceinline__ void pair_halves(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-  return (a & 0xFFFFu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xFFFF0000u);
+__device__ __forceinline__ void wait_vmcnt0() {
+  // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 template <int D, bool kOutBf16, bool kCausal>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const AttnLaunch a) {
+struct Kernel {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::kBufBytes];
+
+  struct State {
+    bf16x8 q[C::kQSteps];
+    f32x16 o[C::kOBlocks];
+    float m;   // running reference max of raw scores q.k
+    float l;   // this lane's partial row sum of fp32 P (its 16 keys of each 32-key block)
+    float lb;  // the same sum over the bf16-rounded P
+  };
+
+  // Per-lane constants of one workgroup.
+  struct Lane {
+    int l32, hi;
+    int k_rd[C::kQSteps];   // K operand read offsets (stage-relative bytes)
+    int v_rd[C::kOBlocks];  // V^T transposing-read offsets (stage-relative bytes)
+    int k_dma[C::kDmaPerWave], v_dma[C::kDmaPerWave];  // global byte offsets within a tile
+    int dma_row0;                                       // tile row of this lane's first DMA chunk
+    int lds_blk0;                                       // wave-uniform LDS offset of its first block
+    int qrow;
+    int hi_lim, sink_lim, win_lo;  // mask: j <= hi_lim and (j < sink_lim or j >= win_lo)
+  };
+
+  // DMA lane mapping: the i-th 1 KiB block of this wave covers tile rows
+  // [row0 + i * rows/block, ...); lane l carries row row0 + i * rows/block +
+  // l / chunks, chunk position l % chunks, i.e. source chunk (l % chunks) ^ swz(row).
+  static __device__ __forceinline__ void issue_dma(char LDS_AS* stage, const Lane& ln, int lane,
+                                                   const char* kt_base, const char* vt_base,
+                                                   int valid_rows, int64_t ks_b, int64_t vs_b) {
+    const bool tail = valid_rows < kBlockK;  // wave-uniform
+#pragma unroll
+    for (int i = 0; i < C::kDmaPerWave; ++i) {
+      int ko = ln.k_dma[i], vo = ln.v_dma[i];
+      if (tail) {  // rows past the sequence end re-read the last row (masked later)
+        const int row = ln.dma_row0 + i * C::kRowsPerBlock;
+        if (row >= valid_rows) {
+          const int r = valid_rows - 1, p = lane % C::kChunks;
+          ko = static_cast<int>(r * ks_b) + (p ^ swz_k<D>(row)) * 16;
+          vo = static_cast<int>(r * vs_b) + (p ^ swz_v<D>(row)) * 16;
+        }
+      }
+      const int blk = ln.lds_blk0 + i * 1024;
+      __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(kt_base + ko),
+                                       (LDS_AS void*)(stage + blk), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(vt_base + vo),
+                                       (LDS_AS void*)(stage + C::kTileBytes + blk), 16, 0, 0);
+    }
+  }
+
+  // One 32-key half (kb) of a tile: S^T block, mask, online softmax, PV.
+  template <bool kPartial>
+  static __device__ __forceinline__ void compute_half(const char LDS_AS* stage, const Lane& ln,
+                                                      State& st, int kb, int key0, float c_log2,
+                                                      float tau_raw) {
+    // S^T = K . Q^T : lane = query, 16 of the 32 keys per lane
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+#pragma unroll
+    for (int q = 0; q < C::kQSteps; ++q) {
+      const bf16x8 kv = *reinterpret_cast<const LDS_AS bf16x8*>(stage + ln.k_rd[q] + kb * 32 * C::kRowBytes);
+      s = mfma32(kv, st.q[q], s);
+    }
+
+    if (kPartial) {
+      // key of register r: key0 + 32 kb + 8 (r >> 2) + 4 hi + (r & 3)
+      const int base = key0 + kb * 32 + ln.hi * 4;
+      const int a = ln.hi_lim - base, sl = ln.sink_lim - base, wl = ln.win_lo - base;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int o = (r >> 2) * 8 + (r & 3);
+        const bool ok = (o <= a) & ((o < sl) | (o >= wl));
+        s[r] = ok ? s[r] : -INFINITY;
+      }
+    }
+
+    // row max over the 32 keys (16 here, 16 in lane ^ 32)
+    float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    {
+      float a0, a1;
+      pair_halves(mx, a0, a1);
+      mx = fmaxf(a0, a1);
+    }
+    // lazy rescale: move the reference max only when some row needs it
+    if (__ballot(mx > st.m + tau_raw) != 0) {
+      const float m_new = fmaxf(st.m, mx);
+      // 0 when st.m = -inf < m_new; 1 when the row is still empty (both -inf)
+      const float alpha = st.m == m_new ? 1.0f : __builtin_amdgcn_exp2f((st.m - m_new) * c_log2);
+      st.m = m_new;
+      st.l *= alpha;
+      st.lb *= alpha;
+#pragma unroll
+      for (int i = 0; i < C::kOBlocks; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.o[i][r] *= alpha;
+    }
+    const float neg_mc = st.m == -INFINITY ? 0.0f : -st.m * c_log2;
+
+    // P = exp2(s c - m c) as packed bf16; 16-key step kc = registers 8 kc .. 8 kc + 7.
+    // Two row sums: of the fp32 P (plain fp32 adds) for the LSE, and of the
+    // bf16 P the PV product actually uses (v_dot2_f32_bf16, 16-term chains)
+    // to normalise O, so that the output weights sum to one exactly.
+    bf16x8 pb[2];
+    float rs = 0.0f;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kc * 8 + x], c_log2, neg_mc));
+        rs += p;
+        pb[kc][x] = static_cast<__bf16>(p);
+      }
+    st.l += rs;
+    float rb = 0.0f;
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const bf16x2 pr = {pb[kc][2 * x], pb[kc][2 * x + 1]};
+        rb = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rb, false);
+      }
+    st.lb += rb;
+
+    // O^T += V^T . P^T ; V^T operand from two transposing reads per 16-key step
+    const char LDS_AS* vst = stage + C::kTileBytes + kb * 32 * C::kRowBytes;
+#pragma unroll
+    for (int ob = 0; ob < C::kOBlocks; ++ob)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS i16x4*)(vst + ln.v_rd[ob] + (kc * 16) * C::kRowBytes));
+        const i16x4 hv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS i16x4*)(vst + ln.v_rd[ob] + (kc * 16 + 8) * C::kRowBytes));
+        // concatenate as integers: element-wise bf16 inserts of the 16-bit lanes
+        // are mis-selected by this compiler (they duplicate lane 0)
+        const u32x2 w0 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 w1 = __builtin_bit_cast(u32x2, hv);
+        const u32x4 w = {w0[0], w0[1], w1[0], w1[1]};
+        st.o[ob] = mfma32(__builtin_bit_cast(bf16x8, w), pb[kc], st.o[ob]);
+      }
+  }
+
+  template <bool kPartial>
+  static __device__ __forceinline__ void compute_tile(const char LDS_AS* stage, const Lane& ln,
+                                                      State& st, int key0, float c_log2,
+                                                      float tau_raw) {
+    compute_half<kPartial>(stage, ln, st, 0, key0, c_log2, tau_raw);
+    compute_half<kPartial>(stage, ln, st, 1, key0, c_log2, tau_raw);
+  }
+};
+
+template <int D, bool kOutBf16, bool kCausal>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const AttnLaunch a) {
+  using K = Kernel<D, kOutBf16, kCausal>;
+  using C = Cfg<D>;
+  // two K/V stages; distinct objects so the DMA into one is known not to alias reads of the other
+  __shared__ __attribute__((aligned(1024))) char smem0[2 * C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char smem1[2 * C::kTileBytes];
+  char LDS_AS* stage0 = (char LDS_AS*)smem0;
+  char LDS_AS* stage1 = (char LDS_AS*)smem1;
 
   const WorkItem w = schedule_item(a.sched, blockIdx.x);
   if (w.t < 0) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int N = a.seqlen;
-  const int G = a.sched.group;
-  const int g = w.h / G;
+  const int g = w.h / a.sched.group;
   const int q0 = w.t * kBlockQ;
-  const int qrow = q0 + wave * 32 + l32;
 
-  const uint16_t* qbase = static_cast<const uint16_t*>(a.q) + w.b * a.q_stride[0] + w.h * a.q_stride[1];
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + w.b * a.k_stride[0] + g * a.k_stride[1];
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + w.b * a.v_stride[0] + g * a.v_stride[1];
-  const int64_t ks_n = a.k_stride[2];
-  const int64_t vs_n = a.v_stride[2];
+  typename K::Lane ln;
+  ln.l32 = lane & 31;
+  ln.hi = lane >> 5;
+  ln.qrow = q0 + wave * 32 + ln.l32;
+
+  const int64_t ks_b = a.k_stride[2] * 2;  // token strides in bytes
+  const int64_t vs_b = a.v_stride[2] * 2;
+  const char* kbase = static_cast<const char*>(a.k) + (w.b * a.k_stride[0] + g * a.k_stride[1]) * 2;
+  const char* vbase = static_cast<const char*>(a.v) + (w.b * a.v_stride[0] + g * a.v_stride[1]) * 2;
+
+  // operand read offsets
+#pragma unroll
+  for (int q = 0; q < C::kQSteps; ++q)
+    ln.k_rd[q] = ln.l32 * C::kRowBytes + (((2 * q + ln.hi) ^ swz_k<D>(ln.l32)) * 16);
+  {
+    const int G = lane >> 4, i = lane & 15, kq = i >> 2, r = i & 3;
+    const int key = (G >> 1) * 4 + kq;  // + 16 kc + 8 x, which leave the swizzle unchanged
+#pragma unroll
+    for (int ob = 0; ob < C::kOBlocks; ++ob) {
+      const int chunk = ob * 4 + 2 * (G & 1) + (r >> 1);
+      ln.v_rd[ob] = key * C::kRowBytes + ((chunk ^ swz_v<D>(key)) * 16) + (r & 1) * 8;
+    }
+  }
+  // DMA lane mapping (see issue_dma)
+  ln.dma_row0 = wave * C::kDmaPerWave * C::kRowsPerBlock + lane / C::kChunks;
+  ln.lds_blk0 = wave * C::kDmaPerWave * 1024;
+#pragma unroll
+  for (int i = 0; i < C::kDmaPerWave; ++i) {
+    const int row = ln.dma_row0 + i * C::kRowsPerBlock;
+    const int p = lane % C::kChunks;
+    ln.k_dma[i] = static_cast<int>(row * ks_b) + (p ^ swz_k<D>(row)) * 16;
+    ln.v_dma[i] = static_cast<int>(row * vs_b) + (p ^ swz_v<D>(row)) * 16;
+  }
+
+  // mask bounds of this lane's row: j <= hi_lim and (j < sink_lim or j >= win_lo)
+  ln.hi_lim = min(ln.qrow, N - 1);
+  if (kCausal || ln.qrow >= N - a.last_q) {
+    ln.sink_lim = 0;
+    ln.win_lo = 0;
+  } else {
+    ln.sink_lim = a.sink;
+    ln.win_lo = ln.qrow - a.window + 1;
+  }
 
   // kept tiles of this query tile
   int e_begin, e_end;
@@ -107,188 +319,102 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const AttnLaunch 
     e_begin = a.row_ptr[w.t];
     e_end = a.row_ptr[w.t + 1];
   }
-
-  // Q^T operand: lane holds Q[qrow][16*s + 8*hi .. +7] for every k-step s.
-  bf16x8 qreg[C::kQSteps];
-  {
-    const uint16_t* qp = qbase + static_cast<int64_t>(qrow) * a.q_stride[2] + hi * 8;
-#pragma unroll
-    for (int s = 0; s < C::kQSteps; ++s) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (qrow < N) x = *reinterpret_cast<const u32x4*>(qp + s * 16);
-      qreg[s] = __builtin_bit_cast(bf16x8, x);
-    }
-  }
-
-  // Global -> register prefetch of one K/V tile.
-  //   K: chunk c = r*256 + tid -> key c / (D/8), 8 channels at 8*(c % (D/8)).
-  //   V: unit tid -> keys 4*(tid%16)..+3, channels 8*(tid/16)..+7.
-  u32x4 kpre[C::kKLoads];
-  u32x4 vpre[4];
-  const int v_kq = tid & 15;
-  const int v_dq = tid >> 4;
-  const bool v_active = tid < C::kVUnits;
-  auto gload = [&](int kt) {
-    const int key0 = kt * kBlockK;
-#pragma unroll
-    for (int r = 0; r < C::kKLoads; ++r) {
-      const int c = r * kThreads + tid;
-      const int key = key0 + c / (D / 8);
-      const int col = (c % (D / 8)) * 8;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < N) x = *reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(key) * ks_n + col);
-      kpre[r] = x;
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = key0 + v_kq * 4 + r;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (v_active && key < N)
-        x = *reinterpret_cast<const u32x4*>(vbase + static_cast<int64_t>(key) * vs_n + v_dq * 8);
-      vpre[r] = x;
+  // tile list in registers, 64 entries per batch (lane i holds entry e0 + i)
+  int list_e0 = e_begin;
+  int list_kt = 0, list_fl = 0;
+  auto load_list = [&](int e0) {
+    list_e0 = e0;
+    if (!kCausal) {
+      const int e = e0 + lane;
+      list_kt = e < e_end ? a.k_tile[e] : 0;
+      list_fl = e < e_end ? a.flags[e] : 0;
     }
   };
-  auto tile_of = [&](int e) -> int { return kCausal ? e : a.k_tile[e]; };
-
-  // mask constants (triangle predicate: j <= i, j < N and (j < sink or
-  // i - j < window or i >= N - last_q))
-  const int last_start = N - a.last_q;
-  const float c_log2 = a.scale * kLog2e;
-
-  f32x16 oacc[C::kOBlocks];
-#pragma unroll
-  for (int i = 0; i < C::kOBlocks; ++i)
-    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
-  float m_i = -INFINITY;  // running max of raw scores q.k
-  float l_i = 0.0f;       // this lane's partial sum (its 16 keys of each block)
-
-  if (e_begin < e_end) gload(tile_of(e_begin));
-
-  for (int e = e_begin; e < e_end; ++e) {
-    char* buf = smem + ((e - e_begin) & 1) * C::kBufBytes;
-    const int kt = tile_of(e);
-    bool partial;
+  auto tile_of = [&](int e) -> int {
+    return kCausal ? e : __builtin_amdgcn_readlane(list_kt, e - list_e0);
+  };
+  auto partial_of = [&](int e, int kt) -> bool {
     if (kCausal) {
       const int c1 = kt * kBlockK + kBlockK - 1;
-      partial = c1 > q0 || c1 >= N;
-    } else {
-      partial = a.flags[e] != TRI_TILE_FULL;
+      return c1 > q0 || c1 >= N;
     }
+    return __builtin_amdgcn_readlane(list_fl, e - list_e0) != TRI_TILE_FULL;
+  };
 
-    // stage the prefetched tile in LDS
+  typename K::State st;
+  {
+    const int qr = ln.qrow;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + w.b * a.q_stride[0] + w.h * a.q_stride[1] +
+                         static_cast<int64_t>(qr) * a.q_stride[2] + ln.hi * 8;
 #pragma unroll
-    for (int r = 0; r < C::kKLoads; ++r) {
-      const int c = r * kThreads + tid;
-      *reinterpret_cast<u32x4*>(buf + (c / (D / 8)) * C::kKStride + (c % (D / 8)) * 16) = kpre[r];
+    for (int q = 0; q < C::kQSteps; ++q) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (qr < N) x = *reinterpret_cast<const u32x4*>(qp + q * 16);
+      st.q[q] = __builtin_bit_cast(bf16x8, x);
     }
-    if (v_active) {
-      char* vt = buf + C::kKBytes + vt_column(v_kq) * 2;
+  }
 #pragma unroll
-      for (int wd = 0; wd < 4; ++wd) {
-        const u32x2 lo = {pack_lo(vpre[0][wd], vpre[1][wd]), pack_lo(vpre[2][wd], vpre[3][wd])};
-        const u32x2 hv = {pack_hi(vpre[0][wd], vpre[1][wd]), pack_hi(vpre[2][wd], vpre[3][wd])};
-        *reinterpret_cast<u32x2*>(vt + (v_dq * 8 + 2 * wd) * C::kVStride) = lo;
-        *reinterpret_cast<u32x2*>(vt + (v_dq * 8 + 2 * wd + 1) * C::kVStride) = hv;
-      }
+  for (int i = 0; i < C::kOBlocks; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.o[i][r] = 0.0f;
+  st.m = -INFINITY;
+  st.l = 0.0f;
+  st.lb = 0.0f;
+
+  const float c_log2 = a.scale * kLog2e;
+  const float tau_raw = kRescaleLog2 / c_log2;
+
+  load_list(e_begin);
+  auto dma = [&](char LDS_AS* stage, int kt) {
+    const int key0 = kt * kBlockK;
+    K::issue_dma(stage, ln, lane, kbase + key0 * ks_b, vbase + key0 * vs_b, N - key0, ks_b, vs_b);
+  };
+  if (e_begin < e_end) dma(stage0, tile_of(e_begin));
+
+  auto step = [&](char LDS_AS* cur, char LDS_AS* nxt, int e) {
+    const int kt = tile_of(e);
+    const bool partial = partial_of(e, kt);
+    wait_vmcnt0();      // this wave's copies of tile e have landed
+    __syncthreads();    // ... and every wave's; all reads of `nxt` (tile e-1) are done
+    if (e + 1 < e_end) {
+      if (e + 1 - list_e0 == 64) load_list(e + 1);
+      dma(nxt, tile_of(e + 1));
     }
-    __syncthreads();
-    if (e + 1 < e_end) gload(tile_of(e + 1));
-
-    // S^T = K . Q^T : two 32-key blocks, lane = query, 16 keys per lane per block
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-      const char* kp = buf + (kb * 32 + l32) * C::kKStride + hi * 16;
-#pragma unroll
-      for (int st = 0; st < C::kQSteps; ++st) {
-        const bf16x8 kv = *reinterpret_cast<const bf16x8*>(kp + st * 32);
-        s[kb] = mfma32(kv, qreg[st], s[kb]);
-      }
-    }
-
-    if (partial) {
-      const int key0 = kt * kBlockK + hi * 4;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = key0 + kb * 32 + (r >> 2) * 8 + (r & 3);
-          bool ok = j <= qrow && j < N;
-          if (!kCausal) ok = ok && (j < a.sink || qrow - j < a.window || qrow >= last_start);
-          if (!ok) s[kb][r] = -INFINITY;
-        }
-    }
-
-    // online softmax (lane-local row statistics; the other 32 keys of the
-    // tile live in lane ^ 32)
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_i, mx);
-    const float m_sub = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f((m_i - m_sub) * c_log2);
-    const float neg_mc = -m_sub * c_log2;
-    float rs = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, neg_mc));
-        s[kb][r] = p;
-        rs += p;
-      }
-    l_i = l_i * alpha + rs;
-    m_i = m_new;
-#pragma unroll
-    for (int i = 0; i < C::kOBlocks; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-
-    // P^T as bf16 B operands: 16-key step kc = registers 8*(kc&1)..+7 of block kc/2
-    bf16x8 pb[4];
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-      for (int x = 0; x < 8; ++x) pb[kc][x] = static_cast<__bf16>(s[kc >> 1][(kc & 1) * 8 + x]);
-
-    // O^T += V^T . P^T
-#pragma unroll
-    for (int ob = 0; ob < C::kOBlocks; ++ob) {
-      const char* vp = buf + C::kKBytes + (ob * 32 + l32) * C::kVStride + hi * 16;
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const bf16x8 vv = *reinterpret_cast<const bf16x8*>(vp + kc * 32);
-        oacc[ob] = mfma32(vv, pb[kc], oacc[ob]);
-      }
-    }
+    if (partial)
+      K::template compute_tile<true>(cur, ln, st, kt * kBlockK, c_log2, tau_raw);
+    else
+      K::template compute_tile<false>(cur, ln, st, kt * kBlockK, c_log2, tau_raw);
+  };
+  for (int e = e_begin; e < e_end; e += 2) {
+    step(stage0, stage1, e);
+    if (e + 1 < e_end) step(stage1, stage0, e + 1);
   }
 
   // epilogue
-  const float l_tot = l_i + __shfl_xor(l_i, 32);
-  if (qrow < N) {
-    const float inv = 1.0f / l_tot;
-    const int64_t orow = w.b * a.o_stride[0] + w.h * a.o_stride[1] + static_cast<int64_t>(qrow) * a.o_stride[2];
+  float l0, l1, b0, b1;
+  pair_halves(st.l, l0, l1);
+  pair_halves(st.lb, b0, b1);
+  const float l_tot = l0 + l1;
+  if (ln.qrow < N) {
+    const float inv = 1.0f / (b0 + b1);
+    const int64_t orow = w.b * a.o_stride[0] + w.h * a.o_stride[1] + static_cast<int64_t>(ln.qrow) * a.o_stride[2];
 #pragma unroll
     for (int ob = 0; ob < C::kOBlocks; ++ob)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = ob * 32 + r4 * 8 + hi * 4;
-        f32x4 v4 = {oacc[ob][r4 * 4 + 0] * inv, oacc[ob][r4 * 4 + 1] * inv,
-                    oacc[ob][r4 * 4 + 2] * inv, oacc[ob][r4 * 4 + 3] * inv};
+        const int d0 = ob * 32 + r4 * 8 + ln.hi * 4;
+        const f32x4 v4 = {st.o[ob][r4 * 4 + 0] * inv, st.o[ob][r4 * 4 + 1] * inv,
+                          st.o[ob][r4 * 4 + 2] * inv, st.o[ob][r4 * 4 + 3] * inv};
         if (kOutBf16) {
-          bf16x4 b4 = {static_cast<__bf16>(v4[0]), static_cast<__bf16>(v4[1]),
-                       static_cast<__bf16>(v4[2]), static_cast<__bf16>(v4[3])};
+          const bf16x4 b4 = {static_cast<__bf16>(v4[0]), static_cast<__bf16>(v4[1]),
+                             static_cast<__bf16>(v4[2]), static_cast<__bf16>(v4[3])};
           *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(a.o) + orow + d0) = b4;
         } else {
           *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + orow + d0) = v4;
         }
       }
-    if (a.lse && hi == 0)
-      a.lse[w.b * a.lse_stride[0] + w.h * a.lse_stride[1] + qrow] = m_i * a.scale + logf(l_tot);
+    if (a.lse && ln.hi == 0)
+      a.lse[w.b * a.lse_stride[0] + w.h * a.lse_stride[1] + ln.qrow] = st.m * a.scale + logf(l_tot);
   }
 }
 

@@ -114,6 +114,12 @@ def test_dense_prefill_rejects_bad_tensors(field, value, status):
     assert tsa.last_error()
 
 
+def test_prefill_rejects_huge_kv_token_stride():
+    t = _good_tensors()
+    t.k_stride[2] = 1 << 24
+    assert _abi.load().dense_causal_prefill(ctypes.byref(t), None) == tsa.TRI_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("which,idx,value", [("q_stride", 2, 100), ("k_stride", 1, 4),
                                              ("v_stride", 0, -8), ("o_stride", 2, 2),
                                              ("lse_stride", 0, -1)])
