@@ -93,8 +93,9 @@ int tri_attn_plan(const tri_mask_params* mp, int32_t* row_ptr, int32_t* k_tile,
 
 /* Device tensors of one layer.  Strides are in elements, for the (batch, head,
  * token) axes; the channel axis is contiguous.  q, k, v are bf16, 16-byte
- * aligned, with token strides that are multiples of 8 elements.  o is bf16
- * (8-byte aligned, token stride a multiple of 4) or f32 (16-byte aligned,
+ * aligned, with token strides that are multiples of 8 elements; the N token
+ * rows of one (batch, KV head) of k and of v must span fewer than 2^31 bytes.
+ * o is bf16 (8-byte aligned, token stride a multiple of 4) or f32 (16-byte aligned,
  * token stride a multiple of 4).  lse (f32) may be NULL. */
 typedef struct {
   const void* q;       /* [B, Hq,  N, d] */

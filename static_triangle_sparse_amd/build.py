@@ -36,24 +36,26 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, lib_path: str = LIB, kernel_src: str = None,
+          build_dir: str = BUILD, extra_hipcc_flags=()) -> str:
+    """Compile and link the library to ``lib_path`` (default: in-tree)."""
+    os.makedirs(build_dir, exist_ok=True)
     hipcc = os.path.join(ROCM, "bin", "hipcc")
     objs = []
     for src in ("plan.cpp", "api.cpp"):
-        obj = os.path.join(BUILD, src + ".o")
+        obj = os.path.join(build_dir, src + ".o")
         _run(["g++", *HOST_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
-    kobj = os.path.join(BUILD, "attn_fwd_gfx950.o")
-    out = _run([hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
-                os.path.join(CSRC, "attn_fwd_gfx950.hip"), "-o", kobj])
+    kobj = os.path.join(build_dir, "attn_fwd_gfx950.o")
+    out = _run([hipcc, *HIPCC_FLAGS, *extra_hipcc_flags, "-I", INCLUDE, "-I", CSRC, "-c",
+                kernel_src or os.path.join(CSRC, "attn_fwd_gfx950.hip"), "-o", kobj])
     if verbose and out.strip():
         print(out)
     objs.append(kobj)
-    tmp = LIB + ".tmp"
+    tmp = lib_path + ".tmp"
     _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

@@ -71,9 +71,11 @@ int validate_tensors(const tri_attn_tensors* t) {
     if (t->o_stride[i] % 4)
       return fail(TRI_ERR_INVALID, "o strides must be multiples of 4 elements");
   }
-  // the kernel addresses one 64-key tile with 32-bit byte offsets
-  if (t->k_stride[2] >= (int64_t(1) << 24) || t->v_stride[2] >= (int64_t(1) << 24))
-    return fail(TRI_ERR_UNSUPPORTED, "k/v token strides must be < 2^24 elements");
+  // the kernel addresses the keys of one (batch, KV head) through 32-bit
+  // buffer descriptors: N token rows of K (and of V) must span < 2^31 bytes
+  if (t->seqlen * t->k_stride[2] * 2 >= (int64_t(1) << 31) ||
+      t->seqlen * t->v_stride[2] * 2 >= (int64_t(1) << 31))
+    return fail(TRI_ERR_UNSUPPORTED, "seqlen x k/v token stride must be < 2^31 bytes");
   if (!aligned(t->o, t->o_dtype == TRI_DTYPE_BF16 ? 8 : 16))
     return fail(TRI_ERR_INVALID, "o must be %d-byte aligned", t->o_dtype == TRI_DTYPE_BF16 ? 8 : 16);
   if (t->lse && !aligned(t->lse, 4)) return fail(TRI_ERR_INVALID, "lse must be 4-byte aligned");

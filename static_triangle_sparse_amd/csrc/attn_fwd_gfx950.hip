@@ -8,9 +8,9 @@
 //   1. K and V are copied HBM -> LDS by the LDS-DMA path
 //      (global_load_lds_dwordx4: each lane's 16 bytes land at LDS base +
 //      16 * lane), double-buffered, one tile ahead of the compute, without
-//      staging registers.  Each 16-byte chunk is placed at an XOR-swizzled
-//      position in its row so that the MFMA operand reads below hit distinct
-//      LDS banks;
+//      staging registers.  Rows are padded (K by 16 bytes, V by 64 bytes) so
+//      the MFMA operand reads below hit distinct LDS banks while every read
+//      address is a per-lane base plus a compile-time offset;
 //   2. S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 (K rows from LDS, Q held in
 //      registers for the whole loop).  Computing the transpose puts one query
 //      per lane, so row statistics are per-lane scalars;
@@ -48,32 +48,31 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBlockQ = TRI_KERNEL_BLOCK_Q;  // 128 query rows per workgroup
 constexpr int kBlockK = TRI_KERNEL_BLOCK_K;  // 64 keys per tile
 constexpr int kThreads = 256;                // 4 waves x 32 query rows
+constexpr int kWaves = kThreads / 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleLog2 = 8.0f;  // rescale when a row max grows by > 2^8 in p units
 
 template <int D>
 struct Cfg {
-  static constexpr int kRowBytes = D * 2;                 // one K or V row
-  static constexpr int kChunks = D / 8;                   // 16-byte chunks per row
-  static constexpr int kTileBytes = kBlockK * kRowBytes;  // one K (or V) tile
-  static constexpr int kRowsPerBlock = 1024 / kRowBytes;  // rows per 1 KiB DMA block
-  static constexpr int kDmaPerWave = kTileBytes / 1024 / 4;  // DMA instructions / wave / matrix
-  static constexpr int kQSteps = D / 16;                  // k-steps of S^T = K Q^T
-  static constexpr int kOBlocks = D / 32;                 // 32-channel blocks of O^T
+  static constexpr int kRowBytes = D * 2;  // data bytes of one K or V row
+  // K rows padded by 16 bytes: the 16 lanes of one S^T operand read (16
+  // consecutive rows, one chunk) then start on distinct banks.
+  static constexpr int kKStride = kRowBytes + 16;
+  // V rows padded by 64 bytes: consecutive rows then start 64 bytes apart
+  // modulo the 256-byte bank window, so the transposing read of a half-wave
+  // (4 rows x 64 bytes) covers every bank once.
+  static constexpr int kVStride = kRowBytes + 64;
+  static constexpr int kKBytes = kBlockK * kKStride;
+  static constexpr int kVBytes = kBlockK * kVStride;
+  static constexpr int kKBlocks = kKBytes / 1024;  // 1 KiB DMA blocks
+  static constexpr int kVBlocks = kVBytes / 1024;
+  static constexpr int kKBlocksPerWave = (kKBlocks + kWaves - 1) / kWaves;
+  static constexpr int kVBlocksPerWave = (kVBlocks + kWaves - 1) / kWaves;
+  static constexpr int kStageBytes = kKBytes + kVBytes;
+  static constexpr int kQSteps = D / 16;   // k-steps of S^T = K Q^T
+  static constexpr int kOBlocks = D / 32;  // 32-channel blocks of O^T
+  static_assert(kKBytes % 1024 == 0 && kVBytes % 1024 == 0, "tiles fill whole DMA blocks");
 };
-
-// Swizzles (16-byte chunk c of tile row r lives at chunk c ^ swz(r)).
-// K: the S^T operand read has 32 lanes on 32 consecutive rows at one chunk;
-// V: the transposing read has each 32-lane half on 4 consecutive rows x 4
-// chunks.  Both place those reads on distinct banks.
-template <int D>
-__device__ __forceinline__ int swz_k(int r) {
-  return D == 128 ? (r & 15) : ((r >> 1) & 7);
-}
-template <int D>
-__device__ __forceinline__ int swz_v(int r) {
-  return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
-}
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -91,6 +90,16 @@ __device__ __forceinline__ void wait_vmcnt0() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+// Tile row and 16-byte source chunk of the DMA chunk that lands at byte x of a
+// tile stored with `stride`-byte padded rows.  Chunks that land on row padding
+// re-read chunk 0 of their row (in bounds, never used).
+template <int D>
+__device__ __forceinline__ void dma_source(int x, int stride, int& row, int& chunk) {
+  row = x / stride;
+  chunk = (x - row * stride) / 16;
+  if (chunk >= D / 8) chunk = 0;
+}
+
 template <int D, bool kOutBf16, bool kCausal>
 struct Kernel {
   using C = Cfg<D>;
@@ -105,39 +114,35 @@ struct Kernel {
 
   // Per-lane constants of one workgroup.
   struct Lane {
-    int l32, hi;
-    int k_rd[C::kQSteps];   // K operand read offsets (stage-relative bytes)
-    int v_rd[C::kOBlocks];  // V^T transposing-read offsets (stage-relative bytes)
-    int k_dma[C::kDmaPerWave], v_dma[C::kDmaPerWave];  // global byte offsets within a tile
-    int dma_row0;                                       // tile row of this lane's first DMA chunk
-    int lds_blk0;                                       // wave-uniform LDS offset of its first block
+    int hi;
+    int k_rd;  // K operand read offset (stage-relative bytes)
+    int v_rd;  // V^T transposing-read offset (relative to the V tile)
+    uint32_t k_dma[C::kKBlocksPerWave];  // global byte offsets within a tile
+    uint32_t v_dma[C::kVBlocksPerWave];
     int qrow;
     int hi_lim, sink_lim, win_lo;  // mask: j <= hi_lim and (j < sink_lim or j >= win_lo)
   };
 
-  // DMA lane mapping: the i-th 1 KiB block of this wave covers tile rows
-  // [row0 + i * rows/block, ...); lane l carries row row0 + i * rows/block +
-  // l / chunks, chunk position l % chunks, i.e. source chunk (l % chunks) ^ swz(row).
-  static __device__ __forceinline__ void issue_dma(char LDS_AS* stage, const Lane& ln, int lane,
-                                                   const char* kt_base, const char* vt_base,
-                                                   int valid_rows, int64_t ks_b, int64_t vs_b) {
-    const bool tail = valid_rows < kBlockK;  // wave-uniform
+  // The i-th DMA block of wave w is block i * waves + w of the tile; lane l of
+  // it fills LDS bytes [16 l, 16 l + 16) of that block.  The copies go through
+  // buffer descriptors that start at the tile and end at the sequence end:
+  // rows past the end are outside the descriptor and land as zeros.
+  static __device__ __forceinline__ void issue_dma(char LDS_AS* stage, const Lane& ln, int wave,
+                                                   __amdgpu_buffer_rsrc_t k_rsrc,
+                                                   __amdgpu_buffer_rsrc_t v_rsrc) {
 #pragma unroll
-    for (int i = 0; i < C::kDmaPerWave; ++i) {
-      int ko = ln.k_dma[i], vo = ln.v_dma[i];
-      if (tail) {  // rows past the sequence end re-read the last row (masked later)
-        const int row = ln.dma_row0 + i * C::kRowsPerBlock;
-        if (row >= valid_rows) {
-          const int r = valid_rows - 1, p = lane % C::kChunks;
-          ko = static_cast<int>(r * ks_b) + (p ^ swz_k<D>(row)) * 16;
-          vo = static_cast<int>(r * vs_b) + (p ^ swz_v<D>(row)) * 16;
-        }
-      }
-      const int blk = ln.lds_blk0 + i * 1024;
-      __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(kt_base + ko),
-                                       (LDS_AS void*)(stage + blk), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(vt_base + vo),
-                                       (LDS_AS void*)(stage + C::kTileBytes + blk), 16, 0, 0);
+    for (int i = 0; i < C::kKBlocksPerWave; ++i) {
+      const int blk = i * kWaves + wave;
+      if (C::kKBlocks % kWaves == 0 || blk < C::kKBlocks)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (LDS_AS void*)(stage + blk * 1024), 16,
+                                                 static_cast<int>(ln.k_dma[i]), 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < C::kVBlocksPerWave; ++i) {
+      const int blk = i * kWaves + wave;
+      if (C::kVBlocks % kWaves == 0 || blk < C::kVBlocks)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (LDS_AS void*)(stage + C::kKBytes + blk * 1024),
+                                                 16, static_cast<int>(ln.v_dma[i]), 0, 0, 0);
     }
   }
 
@@ -147,12 +152,13 @@ struct Kernel {
                                                       State& st, int kb, int key0, float c_log2,
                                                       float tau_raw) {
     // S^T = K . Q^T : lane = query, 16 of the 32 keys per lane
+    const char LDS_AS* kp = stage + ln.k_rd + kb * 32 * C::kKStride;
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.0f;
 #pragma unroll
     for (int q = 0; q < C::kQSteps; ++q) {
-      const bf16x8 kv = *reinterpret_cast<const LDS_AS bf16x8*>(stage + ln.k_rd[q] + kb * 32 * C::kRowBytes);
+      const bf16x8 kv = *reinterpret_cast<const LDS_AS bf16x8*>(kp + q * 32);
       s = mfma32(kv, st.q[q], s);
     }
 
@@ -219,15 +225,15 @@ struct Kernel {
     st.lb += rb;
 
     // O^T += V^T . P^T ; V^T operand from two transposing reads per 16-key step
-    const char LDS_AS* vst = stage + C::kTileBytes + kb * 32 * C::kRowBytes;
+    const char LDS_AS* vp = stage + C::kKBytes + ln.v_rd + kb * 32 * C::kVStride;
 #pragma unroll
     for (int ob = 0; ob < C::kOBlocks; ++ob)
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_AS i16x4*)(vst + ln.v_rd[ob] + (kc * 16) * C::kRowBytes));
+            (LDS_AS i16x4*)(vp + ob * 64 + (kc * 16) * C::kVStride));
         const i16x4 hv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_AS i16x4*)(vst + ln.v_rd[ob] + (kc * 16 + 8) * C::kRowBytes));
+            (LDS_AS i16x4*)(vp + ob * 64 + (kc * 16 + 8) * C::kVStride));
         // concatenate as integers: element-wise bf16 inserts of the 16-bit lanes
         // are mis-selected by this compiler (they duplicate lane 0)
         const u32x2 w0 = __builtin_bit_cast(u32x2, lo);
@@ -251,8 +257,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const AttnLaunch 
   using K = Kernel<D, kOutBf16, kCausal>;
   using C = Cfg<D>;
   // two K/V stages; distinct objects so the DMA into one is known not to alias reads of the other
-  __shared__ __attribute__((aligned(1024))) char smem0[2 * C::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char smem1[2 * C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char smem0[C::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem1[C::kStageBytes];
   char LDS_AS* stage0 = (char LDS_AS*)smem0;
   char LDS_AS* stage1 = (char LDS_AS*)smem1;
 
@@ -265,39 +271,39 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const AttnLaunch 
   const int N = a.seqlen;
   const int g = w.h / a.sched.group;
   const int q0 = w.t * kBlockQ;
+  const int l32 = lane & 31;
 
   typename K::Lane ln;
-  ln.l32 = lane & 31;
   ln.hi = lane >> 5;
-  ln.qrow = q0 + wave * 32 + ln.l32;
+  ln.qrow = q0 + wave * 32 + l32;
 
   const int64_t ks_b = a.k_stride[2] * 2;  // token strides in bytes
   const int64_t vs_b = a.v_stride[2] * 2;
   const char* kbase = static_cast<const char*>(a.k) + (w.b * a.k_stride[0] + g * a.k_stride[1]) * 2;
   const char* vbase = static_cast<const char*>(a.v) + (w.b * a.v_stride[0] + g * a.v_stride[1]) * 2;
 
-  // operand read offsets
-#pragma unroll
-  for (int q = 0; q < C::kQSteps; ++q)
-    ln.k_rd[q] = ln.l32 * C::kRowBytes + (((2 * q + ln.hi) ^ swz_k<D>(ln.l32)) * 16);
+  // operand read offsets: K row l32, channels 8 hi .. 8 hi + 7 (+ 16 per k-step);
+  // V^T transposing read: lane (G = lane / 16, k' = lane % 16 / 4, r = lane % 4)
+  // points at key 4 (G / 2) + k' (+ 16 kc + 8 x), channels 16 (G % 2) + 4 r .. +3
+  // (+ 32 ob).  Destination lane (G, 4 r + c) then receives channel
+  // 16 (G % 2) + 4 r + c of keys 4 (G / 2) + 0..3: the layout of the PV operand.
+  ln.k_rd = l32 * C::kKStride + ln.hi * 16;
   {
-    const int G = lane >> 4, i = lane & 15, kq = i >> 2, r = i & 3;
-    const int key = (G >> 1) * 4 + kq;  // + 16 kc + 8 x, which leave the swizzle unchanged
-#pragma unroll
-    for (int ob = 0; ob < C::kOBlocks; ++ob) {
-      const int chunk = ob * 4 + 2 * (G & 1) + (r >> 1);
-      ln.v_rd[ob] = key * C::kRowBytes + ((chunk ^ swz_v<D>(key)) * 16) + (r & 1) * 8;
-    }
+    const int G = lane >> 4, kq = (lane >> 2) & 3, r = lane & 3;
+    ln.v_rd = ((G >> 1) * 4 + kq) * C::kVStride + (16 * (G & 1) + 4 * r) * 2;
   }
-  // DMA lane mapping (see issue_dma)
-  ln.dma_row0 = wave * C::kDmaPerWave * C::kRowsPerBlock + lane / C::kChunks;
-  ln.lds_blk0 = wave * C::kDmaPerWave * 1024;
+  // DMA sources of this lane (see issue_dma)
 #pragma unroll
-  for (int i = 0; i < C::kDmaPerWave; ++i) {
-    const int row = ln.dma_row0 + i * C::kRowsPerBlock;
-    const int p = lane % C::kChunks;
-    ln.k_dma[i] = static_cast<int>(row * ks_b) + (p ^ swz_k<D>(row)) * 16;
-    ln.v_dma[i] = static_cast<int>(row * vs_b) + (p ^ swz_v<D>(row)) * 16;
+  for (int i = 0; i < C::kKBlocksPerWave; ++i) {
+    int row, chunk;
+    dma_source<D>((i * kWaves + wave) * 1024 + lane * 16, C::kKStride, row, chunk);
+    ln.k_dma[i] = static_cast<uint32_t>(min(row, kBlockK - 1) * ks_b) + chunk * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < C::kVBlocksPerWave; ++i) {
+    int row, chunk;
+    dma_source<D>((i * kWaves + wave) * 1024 + lane * 16, C::kVStride, row, chunk);
+    ln.v_dma[i] = static_cast<uint32_t>(min(row, kBlockK - 1) * vs_b) + chunk * 16;
   }
 
   // mask bounds of this lane's row: j <= hi_lim and (j < sink_lim or j >= win_lo)
@@ -365,17 +371,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const AttnLaunch 
   const float tau_raw = kRescaleLog2 / c_log2;
 
   load_list(e_begin);
+  // buffer flags word for raw (unswizzled, stride 0) descriptors
+  constexpr int kRsrcFlags = 0x00020000;
   auto dma = [&](char LDS_AS* stage, int kt) {
     const int key0 = kt * kBlockK;
-    K::issue_dma(stage, ln, lane, kbase + key0 * ks_b, vbase + key0 * vs_b, N - key0, ks_b, vs_b);
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kbase + key0 * ks_b), 0, static_cast<int>((N - key0) * ks_b), kRsrcFlags);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vbase + key0 * vs_b), 0, static_cast<int>((N - key0) * vs_b), kRsrcFlags);
+    K::issue_dma(stage, ln, wave, kr, vr);
   };
   if (e_begin < e_end) dma(stage0, tile_of(e_begin));
 
   auto step = [&](char LDS_AS* cur, char LDS_AS* nxt, int e) {
     const int kt = tile_of(e);
     const bool partial = partial_of(e, kt);
-    wait_vmcnt0();      // this wave's copies of tile e have landed
-    __syncthreads();    // ... and every wave's; all reads of `nxt` (tile e-1) are done
+    wait_vmcnt0();    // this wave's copies of tile e have landed
+    __syncthreads();  // ... and every wave's; all reads of `nxt` (tile e-1) are done
     if (e + 1 < e_end) {
       if (e + 1 - list_e0 == 64) load_list(e + 1);
       dma(nxt, tile_of(e + 1));
@@ -397,7 +409,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const AttnLaunch 
   const float l_tot = l0 + l1;
   if (ln.qrow < N) {
     const float inv = 1.0f / (b0 + b1);
-    const int64_t orow = w.b * a.o_stride[0] + w.h * a.o_stride[1] + static_cast<int64_t>(ln.qrow) * a.o_stride[2];
+    const int64_t orow =
+        w.b * a.o_stride[0] + w.h * a.o_stride[1] + static_cast<int64_t>(ln.qrow) * a.o_stride[2];
 #pragma unroll
     for (int ob = 0; ob < C::kOBlocks; ++ob)
 #pragma unroll
@@ -420,8 +433,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const AttnLaunch 
 
 template <int D, bool kOutBf16, bool kCausal>
 int launch_t(const AttnLaunch& a, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, kOutBf16, kCausal>), dim3(static_cast<unsigned>(a.sched.grid)),
-                     dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, kOutBf16, kCausal>),
+                     dim3(static_cast<unsigned>(a.sched.grid)), dim3(kThreads), 0, stream, a);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(TRI_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   return TRI_OK;

@@ -114,9 +114,12 @@ def test_dense_prefill_rejects_bad_tensors(field, value, status):
     assert tsa.last_error()
 
 
-def test_prefill_rejects_huge_kv_token_stride():
-    t = _good_tensors()
-    t.k_stride[2] = 1 << 24
+def test_prefill_rejects_keys_spanning_2gib():
+    t = _good_tensors(N=1 << 16)
+    t.k_stride[2] = 1 << 14          # 65536 tokens x 32 KiB = 2 GiB
+    assert _abi.load().dense_causal_prefill(ctypes.byref(t), None) == tsa.TRI_ERR_UNSUPPORTED
+    t.k_stride[2] = 128
+    t.v_stride[2] = 1 << 14
     assert _abi.load().dense_causal_prefill(ctypes.byref(t), None) == tsa.TRI_ERR_UNSUPPORTED
 
 
