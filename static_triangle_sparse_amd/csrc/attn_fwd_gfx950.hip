@@ -4,21 +4,26 @@
 // technical motivation) and the dense causal layer use the same kernel.
 //
 // One workgroup = one (batch, query head, 128-row query tile); 4 waves, each
-// owning 32 query rows; two workgroups share a CU.  Per kept 64-key tile:
-//   1. K and V are copied HBM -> LDS by the LDS-DMA path
-//      (global_load_lds_dwordx4: each lane's 16 bytes land at LDS base +
-//      16 * lane), double-buffered, one tile ahead of the compute, without
-//      staging registers.  Rows are padded (K by 16 bytes, V by 64 bytes) so
-//      the MFMA operand reads below hit distinct LDS banks while every read
-//      address is a per-lane base plus a compile-time offset;
+// owning 32 query rows.  A kept 64-key tile is processed as two 32-key
+// halves, and the LDS stage holds one half (38 KiB for two stages), so three
+// workgroups share a CU: three waves per SIMD keep the matrix cores fed while
+// the others wait on LDS reads, dependent vector instructions or copies.
+// Per 32-key half:
+//   1. K and V are copied HBM -> LDS by the LDS-DMA path (each lane's 16
+//      bytes land at LDS base + 16 * lane), double-buffered, one half ahead of
+//      the compute, without staging registers.  Rows are padded (K by 16
+//      bytes, V by 64 bytes) so the MFMA operand reads below hit distinct LDS
+//      banks while every read address is a per-lane base plus a compile-time
+//      offset;
 //   2. S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 (K rows from LDS, Q held in
 //      registers for the whole loop).  Computing the transpose puts one query
 //      per lane, so row statistics are per-lane scalars;
 //   3. PARTIAL tiles apply the mask predicate per element, FULL tiles skip it;
-//   4. online softmax in fp32 with exp2 (log2 e folded into the scale); the
-//      accumulator is rescaled only when some row's running max grows by more
-//      than 2^8 (softmax is invariant to the reference point, and P stays below
-//      256, far inside fp32/bf16 range);
+//   4. softmax in fp32 with exp2 (log2 e folded into the scale) against a
+//      reference max that is fixed per row by the first block that keeps one
+//      of its keys, so the O accumulators are never rescaled in the loop; a
+//      row whose max later outgrows the reference by more than 2^64 in p
+//      units sends the workgroup through a second pass with exact maxima;
 //   5. O^T += V^T . P^T on MFMA: the fp32 scores of step 2 are already laid out
 //      as the B operand of this product once converted to bf16, so P never
 //      leaves registers; the A operand V^T is read from the row-major V tile
@@ -47,10 +52,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBlockQ = TRI_KERNEL_BLOCK_Q;  // 128 query rows per workgroup
 constexpr int kBlockK = TRI_KERNEL_BLOCK_K;  // 64 keys per tile
+constexpr int kHalf = kBlockK / 2;           // keys per stage
 constexpr int kThreads = 256;                // 4 waves x 32 query rows
 constexpr int kWaves = kThreads / 64;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleLog2 = 8.0f;  // rescale when a row max grows by > 2^8 in p units
+constexpr float kRefSlackLog2 = 64.0f;  // largest p = 2^64 above a row's reference max
 
 template <int D>
 struct Cfg {
@@ -62,8 +68,10 @@ struct Cfg {
   // modulo the 256-byte bank window, so the transposing read of a half-wave
   // (4 rows x 64 bytes) covers every bank once.
   static constexpr int kVStride = kRowBytes + 64;
-  static constexpr int kKBytes = kBlockK * kKStride;
-  static constexpr int kVBytes = kBlockK * kVStride;
+  // a stage holds one 32-key half of a tile (K region rounded up to whole
+  // 1 KiB copy blocks)
+  static constexpr int kKBytes = (kHalf * kKStride + 1023) / 1024 * 1024;
+  static constexpr int kVBytes = kHalf * kVStride;
   static constexpr int kKBlocks = kKBytes / 1024;  // 1 KiB DMA blocks
   static constexpr int kVBlocks = kVBytes / 1024;
   static constexpr int kKBlocksPerWave = (kKBlocks + kWaves - 1) / kWaves;
@@ -107,7 +115,8 @@ struct Kernel {
   struct State {
     bf16x8 q[C::kQSteps];
     f32x16 o[C::kOBlocks];
-    float m;   // running reference max of raw scores q.k
+    float m;   // reference max of raw scores q.k (fixed once set, see compute_half)
+    float mt;  // true running max of raw scores q.k
     float l;   // this lane's partial row sum of fp32 P (its 16 keys of each 32-key block)
     float lb;  // the same sum over the bf16-rounded P
   };
@@ -146,13 +155,20 @@ struct Kernel {
     }
   }
 
-  // One 32-key half (kb) of a tile: S^T block, mask, online softmax, PV.
-  template <bool kPartial>
+  // One 32-key half (kb) of a tile: S^T block, mask, softmax, PV.
+  //
+  // The reference max of a row is fixed by the first block that keeps a key
+  // of it and never moves afterwards, so the O accumulators are never
+  // rescaled inside the loop.  A later block whose max exceeds the reference
+  // by more than 2^kRefSlackLog2 (in p units) flags the wave in `bad`; the
+  // workgroup then runs the loop a second time with each row's exact max
+  // (tracked in mt) as the reference.  Below that bound p <= 2^kRefSlackLog2,
+  // and the fp32 sums stay far inside the exponent range.
   static __device__ __forceinline__ void compute_half(const char LDS_AS* stage, const Lane& ln,
-                                                      State& st, int kb, int key0, float c_log2,
-                                                      float tau_raw) {
+                                                      State& st, int kb, int key0, bool partial,
+                                                      float c_log2, float tau_raw, bool& bad) {
     // S^T = K . Q^T : lane = query, 16 of the 32 keys per lane
-    const char LDS_AS* kp = stage + ln.k_rd + kb * 32 * C::kKStride;
+    const char LDS_AS* kp = stage + ln.k_rd;
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.0f;
@@ -162,7 +178,7 @@ struct Kernel {
       s = mfma32(kv, st.q[q], s);
     }
 
-    if (kPartial) {
+    if (partial) {
       // key of register r: key0 + 32 kb + 8 (r >> 2) + 4 hi + (r & 3)
       const int base = key0 + kb * 32 + ln.hi * 4;
       const int a = ln.hi_lim - base, sl = ln.sink_lim - base, wl = ln.win_lo - base;
@@ -183,21 +199,11 @@ struct Kernel {
       pair_halves(mx, a0, a1);
       mx = fmaxf(a0, a1);
     }
-    // lazy rescale: move the reference max only when some row needs it
-    if (__ballot(mx > st.m + tau_raw) != 0) {
-      const float m_new = fmaxf(st.m, mx);
-      // 0 when st.m = -inf < m_new; 1 when the row is still empty (both -inf)
-      const float alpha = st.m == m_new ? 1.0f : __builtin_amdgcn_exp2f((st.m - m_new) * c_log2);
-      st.m = m_new;
-      st.l *= alpha;
-      st.lb *= alpha;
-#pragma unroll
-      for (int i = 0; i < C::kOBlocks; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st.o[i][r] *= alpha;
-    }
+    st.mt = fmaxf(st.mt, mx);
+    // a row with no kept key so far has O = 0 and l = 0: its reference may still move
+    if (st.m == -INFINITY) st.m = mx;
+    bad |= __ballot(mx > st.m + tau_raw) != 0;
     const float neg_mc = st.m == -INFINITY ? 0.0f : -st.m * c_log2;
-
     // P = exp2(s c - m c) as packed bf16; 16-key step kc = registers 8 kc .. 8 kc + 7.
     // Two row sums: of the fp32 P (plain fp32 adds) for the LSE, and of the
     // bf16 P the PV product actually uses (v_dot2_f32_bf16, 16-term chains)
@@ -225,7 +231,7 @@ struct Kernel {
     st.lb += rb;
 
     // O^T += V^T . P^T ; V^T operand from two transposing reads per 16-key step
-    const char LDS_AS* vp = stage + C::kKBytes + ln.v_rd + kb * 32 * C::kVStride;
+    const char LDS_AS* vp = stage + C::kKBytes + ln.v_rd;
 #pragma unroll
     for (int ob = 0; ob < C::kOBlocks; ++ob)
 #pragma unroll
@@ -243,24 +249,21 @@ struct Kernel {
       }
   }
 
-  template <bool kPartial>
   static __device__ __forceinline__ void compute_tile(const char LDS_AS* stage, const Lane& ln,
-                                                      State& st, int key0, float c_log2,
-                                                      float tau_raw) {
-    compute_half<kPartial>(stage, ln, st, 0, key0, c_log2, tau_raw);
-    compute_half<kPartial>(stage, ln, st, 1, key0, c_log2, tau_raw);
+                                                      State& st, int key0, bool partial,
+                                                      float c_log2, float tau_raw, bool& bad) {
+    compute_half(stage, ln, st, 0, key0, partial, c_log2, tau_raw, bad);
+    compute_half(stage, ln, st, 1, key0, partial, c_log2, tau_raw, bad);
   }
 };
 
 template <int D, bool kOutBf16, bool kCausal>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const AttnLaunch a) {
+__global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch a) {
   using K = Kernel<D, kOutBf16, kCausal>;
   using C = Cfg<D>;
-  // two K/V stages; distinct objects so the DMA into one is known not to alias reads of the other
-  __shared__ __attribute__((aligned(1024))) char smem0[C::kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char smem1[C::kStageBytes];
-  char LDS_AS* stage0 = (char LDS_AS*)smem0;
-  char LDS_AS* stage1 = (char LDS_AS*)smem1;
+  // two K/V stages
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * C::kStageBytes];
+  char LDS_AS* smem = (char LDS_AS*)smem_raw;
 
   const WorkItem w = schedule_item(a.sched, blockIdx.x);
   if (w.t < 0) return;
@@ -297,13 +300,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const AttnLaunch 
   for (int i = 0; i < C::kKBlocksPerWave; ++i) {
     int row, chunk;
     dma_source<D>((i * kWaves + wave) * 1024 + lane * 16, C::kKStride, row, chunk);
-    ln.k_dma[i] = static_cast<uint32_t>(min(row, kBlockK - 1) * ks_b) + chunk * 16;
+    ln.k_dma[i] = static_cast<uint32_t>(min(row, kHalf - 1) * ks_b) + chunk * 16;
   }
 #pragma unroll
   for (int i = 0; i < C::kVBlocksPerWave; ++i) {
     int row, chunk;
     dma_source<D>((i * kWaves + wave) * 1024 + lane * 16, C::kVStride, row, chunk);
-    ln.v_dma[i] = static_cast<uint32_t>(min(row, kBlockK - 1) * vs_b) + chunk * 16;
+    ln.v_dma[i] = static_cast<uint32_t>(min(row, kHalf - 1) * vs_b) + chunk * 16;
   }
 
   // mask bounds of this lane's row: j <= hi_lim and (j < sink_lim or j >= win_lo)
@@ -359,47 +362,58 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const AttnLaunch 
       st.q[q] = __builtin_bit_cast(bf16x8, x);
     }
   }
-#pragma unroll
-  for (int i = 0; i < C::kOBlocks; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) st.o[i][r] = 0.0f;
   st.m = -INFINITY;
-  st.l = 0.0f;
-  st.lb = 0.0f;
+  st.mt = -INFINITY;
 
   const float c_log2 = a.scale * kLog2e;
-  const float tau_raw = kRescaleLog2 / c_log2;
+  const float tau_raw = kRefSlackLog2 / c_log2;
 
-  load_list(e_begin);
   // buffer flags word for raw (unswizzled, stride 0) descriptors
   constexpr int kRsrcFlags = 0x00020000;
-  auto dma = [&](char LDS_AS* stage, int kt) {
-    const int key0 = kt * kBlockK;
+  auto dma = [&](char LDS_AS* stage, int kt, int kb) {
+    const int key0 = kt * kBlockK + kb * kHalf;
+    // keys past the sequence end (the second half of a last tile can start
+    // there) are outside the descriptor and land as zeros
+    const int rows = max(N - key0, 0);
     const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kbase + key0 * ks_b), 0, static_cast<int>((N - key0) * ks_b), kRsrcFlags);
+        (void*)(kbase + key0 * ks_b), 0, static_cast<int>(rows * ks_b), kRsrcFlags);
     const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vbase + key0 * vs_b), 0, static_cast<int>((N - key0) * vs_b), kRsrcFlags);
+        (void*)(vbase + key0 * vs_b), 0, static_cast<int>(rows * vs_b), kRsrcFlags);
     K::issue_dma(stage, ln, wave, kr, vr);
   };
-  if (e_begin < e_end) dma(stage0, tile_of(e_begin));
 
-  auto step = [&](char LDS_AS* cur, char LDS_AS* nxt, int e) {
-    const int kt = tile_of(e);
-    const bool partial = partial_of(e, kt);
-    wait_vmcnt0();    // this wave's copies of tile e have landed
-    __syncthreads();  // ... and every wave's; all reads of `nxt` (tile e-1) are done
-    if (e + 1 < e_end) {
-      if (e + 1 - list_e0 == 64) load_list(e + 1);
-      dma(nxt, tile_of(e + 1));
+  for (int pass = 0;; ++pass) {
+#pragma unroll
+    for (int i = 0; i < C::kOBlocks; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[i][r] = 0.0f;
+    st.l = 0.0f;
+    st.lb = 0.0f;
+    bool bad = false;
+
+    load_list(e_begin);
+    if (e_begin < e_end) dma(smem, tile_of(e_begin), 0);
+    int cur = 0;  // byte offset of the stage holding the current half
+    for (int e = e_begin; e < e_end; ++e) {
+      const int kt = tile_of(e);
+      const bool partial = partial_of(e, kt);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        wait_vmcnt0();    // this wave's copies of this half have landed
+        __syncthreads();  // ... and every wave's; all reads of the other stage are done
+        if (kb == 0) {
+          dma(smem + (cur ^ C::kStageBytes), kt, 1);
+        } else if (e + 1 < e_end) {
+          if (e + 1 - list_e0 == 64) load_list(e + 1);
+          dma(smem + (cur ^ C::kStageBytes), tile_of(e + 1), 0);
+        }
+        K::compute_half(smem + cur, ln, st, kb, kt * kBlockK, partial, c_log2, tau_raw, bad);
+        cur ^= C::kStageBytes;
+      }
     }
-    if (partial)
-      K::template compute_tile<true>(cur, ln, st, kt * kBlockK, c_log2, tau_raw);
-    else
-      K::template compute_tile<false>(cur, ln, st, kt * kBlockK, c_log2, tau_raw);
-  };
-  for (int e = e_begin; e < e_end; e += 2) {
-    step(stage0, stage1, e);
-    if (e + 1 < e_end) step(stage1, stage0, e + 1);
+    // second pass (rare): some row's max outgrew its reference; rerun with the exact maxima
+    if (pass == 1 || !__syncthreads_or(bad)) break;
+    st.m = st.mt;
   }
 
   // epilogue
