@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "tri_attn_internal.h"
 
 namespace triattn {
@@ -57,7 +59,8 @@ constexpr int kHalf = kBlockK / 2;           // keys per stage
 constexpr int kThreads = 256;                // 4 waves x 32 query rows
 constexpr int kWaves = kThreads / 64;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRefSlackLog2 = 64.0f;  // largest p = 2^64 above a row's reference max
+constexpr float kSumLimit = 0x1p64f;  // a row sum of P above this sends the workgroup to the exact-max passes
+constexpr uint32_t kNegInfBits = 0xFF800000u;
 
 template <int D>
 struct Cfg {
@@ -92,6 +95,56 @@ __device__ __forceinline__ void pair_halves(float x, float& lo, float& hi) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   lo = __uint_as_float(r[0]);
   hi = __uint_as_float(r[1]);
+}
+
+// Max of finite or -inf scores.  Written as assembly: the compiler's fmaxf
+// first quiets each operand (v_max_f32 x, x) because it cannot prove the
+// MFMA results are not signalling NaNs.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmax2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// Bits [0, x) set, for any x (none for x <= 0, all for x >= 32): the bit
+// field mask of min(max(x, 0), 31) bits, or'ed with all ones when x > 31.
+// Assembly, because the compiler rewrites the sign trick into a compare and
+// a select.
+__device__ __forceinline__ uint32_t low_bits(int x) {
+  uint32_t r, t, u;
+  asm("v_med3_i32 %1, %3, 0, 31\n\t"
+      "v_bfm_b32 %1, %1, 0\n\t"
+      "v_sub_u32 %2, 31, %3\n\t"
+      "v_ashrrev_i32 %2, 31, %2\n\t"
+      "v_or_b32 %0, %1, %2"
+      : "=v"(r), "=&v"(t), "=&v"(u)
+      : "v"(x));
+  return r;
+}
+
+// s, or -inf where bit O of `drop` is set: a sign-extended one-bit field
+// selects the -inf pattern bit by bit (two full-rate instructions instead of
+// a compare and a select).
+template <int O>
+__device__ __forceinline__ float drop_if(float s, uint32_t drop, uint32_t neg_inf_bits) {
+  uint32_t m, r = __float_as_uint(s);
+  asm("v_bfe_i32 %0, %2, %3, 1\n\t"
+      "v_bfi_b32 %1, %0, %4, %1"
+      : "=&v"(m), "+v"(r)
+      : "v"(drop), "i"(O), "s"(neg_inf_bits));
+  return __uint_as_float(r);
+}
+
+// Register r of a score block holds key offset 8 (r >> 2) + (r & 3) (+ 4 for
+// the upper half-wave, removed by the caller's shift of `drop`).
+template <int... R>
+__device__ __forceinline__ void drop_keys(float (&s)[16], uint32_t drop, std::integer_sequence<int, R...>) {
+  ((s[R] = drop_if<(R >> 2) * 8 + (R & 3)>(s[R], drop, kNegInfBits)), ...);
 }
 
 __device__ __forceinline__ void wait_vmcnt0() {
@@ -140,8 +193,9 @@ struct Kernel {
   struct State {
     bf16x8 q[C::kQSteps];
     f32x16 o[C::kOBlocks];
-    float m;   // reference max of raw scores q.k (fixed once set, see compute_half)
-    float mt;  // true running max of raw scores q.k
+    float m;       // reference max of raw scores q.k (fixed once set, see compute_half)
+    float neg_mc;  // -m c log2(e), or 0 while m is unset
+    float mt;      // true running max of raw scores q.k (exact-max pass only)
     float l;   // this lane's partial row sum of fp32 P (its 16 keys of each 32-key block)
     float lb;  // the same sum over the bf16-rounded P
   };
@@ -202,19 +256,11 @@ struct Kernel {
     }
   }
 
-  // One 32-key half (kb) of a tile: S^T block, mask, softmax, PV.
-  //
-  // The reference max of a row is fixed by the first block that keeps a key
-  // of it and never moves afterwards, so the O accumulators are never
-  // rescaled inside the loop.  A later block whose max exceeds the reference
-  // by more than 2^kRefSlackLog2 (in p units) flags the wave in `bad`; the
-  // workgroup then runs the loop a second time with each row's exact max
-  // (tracked in mt) as the reference.  Below that bound p <= 2^kRefSlackLog2,
-  // and the fp32 sums stay far inside the exponent range.
-  static __device__ __forceinline__ void compute_half(const char LDS_AS* stage, const Lane& ln,
-                                                      State& st, int kb, int key0, bool partial,
-                                                      float c_log2, float tau_raw, bool& bad) {
-    // S^T = K . Q^T : lane = query, 16 of the 32 keys per lane
+  // S^T block of one 32-key half (kb): lane = query, 16 of the 32 keys per
+  // lane; register r holds key key0 + 32 kb + 8 (r >> 2) + 4 hi + (r & 3).
+  // Keys a PARTIAL tile drops are set to -inf.
+  static __device__ __forceinline__ f32x16 scores(const char LDS_AS* stage, const Lane& ln, const State& st,
+                                                  int kb, int key0, bool partial) {
     const char LDS_AS* kp = stage + ln.k_rd;
     f32x16 s;
 #pragma unroll
@@ -224,65 +270,92 @@ struct Kernel {
       const bf16x8 kv = *reinterpret_cast<const LDS_AS bf16x8*>(kp + q * 32);
       s = mfma32(kv, st.q[q], s);
     }
-
     if (partial) {
-      // key of register r: key0 + 32 kb + 8 (r >> 2) + 4 hi + (r & 3)
-      const int base = key0 + kb * 32 + ln.hi * 4;
-      const int a = ln.hi_lim - base, sl = ln.sink_lim - base, wl = ln.win_lo - base;
+      // bit o of `drop` is set when key base + o is masked for this lane's row
+      const int base = key0 + kb * 32;
+      const uint32_t keep = low_bits(ln.hi_lim - base + 1) &
+                            (low_bits(ln.sink_lim - base) | ~low_bits(ln.win_lo - base));
+      const uint32_t drop = ~keep >> (ln.hi * 4);
+      float sv[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int o = (r >> 2) * 8 + (r & 3);
-        const bool ok = (o <= a) & ((o < sl) | (o >= wl));
-        s[r] = ok ? s[r] : -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r) sv[r] = s[r];
+      drop_keys(sv, drop, std::make_integer_sequence<int, 16>());
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = sv[r];
     }
+    return s;
+  }
 
-    // row max over the 32 keys (16 here, 16 in lane ^ 32)
-    float mx = fmaxf(s[0], s[1]);
-#pragma unroll
-    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    {
-      float a0, a1;
-      pair_halves(mx, a0, a1);
-      mx = fmaxf(a0, a1);
+  // Row max over the 32 keys of a score block (16 here, 16 in lane ^ 32).
+  static __device__ __forceinline__ float row_max(const f32x16& s) {
+    const float a0 = vmax3(s[0], s[1], s[2]), a1 = vmax3(s[3], s[4], s[5]);
+    const float a2 = vmax3(s[6], s[7], s[8]), a3 = vmax3(s[9], s[10], s[11]);
+    const float a4 = vmax3(s[12], s[13], s[14]);
+    const float mx = vmax2(vmax3(a0, a1, a2), vmax3(a3, a4, s[15]));
+    float h0, h1;
+    pair_halves(mx, h0, h1);
+    return vmax2(h0, h1);
+  }
+
+  // One 32-key half (kb) of a tile: S^T block, mask, softmax, PV.
+  //
+  // The reference max of a row is fixed by the first block that keeps a key
+  // of it and never moves afterwards, so the O accumulators are never
+  // rescaled and, once every row of the wave has its reference (need_ref
+  // false), no max is taken at all.  P = exp2(s c - m c) can then exceed 1
+  // when a later key outscores the reference; the caller checks the row
+  // sums at the end and, if any exceeds kSumLimit (so some P may have lost
+  // range), reruns the list with each row's exact max as the reference.
+  static __device__ __forceinline__ void compute_half(const char LDS_AS* stage, const Lane& ln,
+                                                      State& st, int kb, int key0, bool partial,
+                                                      float c_log2, bool& need_ref) {
+    const f32x16 s = scores(stage, ln, st, kb, key0, partial);
+    if (need_ref) {
+      // a row with no kept key so far has O = 0 and l = 0: its reference may still move
+      const float mx = row_max(s);
+      if (st.m == -INFINITY && mx != -INFINITY) {
+        st.m = mx;
+        st.neg_mc = -mx * c_log2;
+      }
+      need_ref = __ballot(st.m == -INFINITY) != 0;
     }
-    st.mt = fmaxf(st.mt, mx);
-    // a row with no kept key so far has O = 0 and l = 0: its reference may still move
-    if (st.m == -INFINITY) st.m = mx;
-    bad |= __ballot(mx > st.m + tau_raw) != 0;
-    const float neg_mc = st.m == -INFINITY ? 0.0f : -st.m * c_log2;
     // P = exp2(s c - m c) as packed bf16; 16-key step kc = registers 8 kc .. 8 kc + 7.
-    // Two row sums: of the fp32 P (plain fp32 adds) for the LSE, and of the
-    // bf16 P the PV product actually uses (v_dot2_f32_bf16, 16-term chains)
-    // to normalise O, so that the output weights sum to one exactly.
+    // Two row sums: of the fp32 P for the LSE, and of the bf16 P the PV
+    // product actually uses (v_dot2_f32_bf16) to normalise O, so that the
+    // output weights sum to one exactly.  Pairwise trees keep the dependent
+    // chains short.
     bf16x8 pb[2];
-    float rs = 0.0f;
+    float pf[16];
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kc * 8 + x], c_log2, neg_mc));
-        rs += p;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kc * 8 + x], c_log2, st.neg_mc));
+        pf[kc * 8 + x] = p;
         pb[kc][x] = static_cast<__bf16>(p);
       }
-    st.l += rs;
-    float rb = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) pf[r] += pf[r + 8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pf[r] += pf[r + 4];
+    st.l += (pf[0] + pf[2]) + (pf[1] + pf[3]);
+    float rb[2] = {0.0f, 0.0f};
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const bf16x2 pr = {pb[kc][2 * x], pb[kc][2 * x + 1]};
-        rb = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rb, false);
+        rb[kc] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rb[kc], false);
       }
-    st.lb += rb;
+    st.lb += rb[0] + rb[1];
 
     // O^T += V^T . P^T ; V^T operand from two transposing reads per 16-key step
     const char LDS_AS* vp = stage + C::kKBytes + ln.v_rd;
 #pragma unroll
-    for (int ob = 0; ob < C::kOBlocks; ++ob)
+    for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
+      for (int ob = 0; ob < C::kOBlocks; ++ob) {
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (LDS_AS i16x4*)(vp + ob * 64 + (kc * 16) * C::kVStride));
         const i16x4 hv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -296,11 +369,10 @@ struct Kernel {
       }
   }
 
-  static __device__ __forceinline__ void compute_tile(const char LDS_AS* stage, const Lane& ln,
-                                                      State& st, int key0, bool partial,
-                                                      float c_log2, float tau_raw, bool& bad) {
-    compute_half(stage, ln, st, 0, key0, partial, c_log2, tau_raw, bad);
-    compute_half(stage, ln, st, 1, key0, partial, c_log2, tau_raw, bad);
+  // Exact-max pass over one 32-key half: scores and row max only.
+  static __device__ __forceinline__ void max_half(const char LDS_AS* stage, const Lane& ln, State& st, int kb,
+                                                  int key0, bool partial) {
+    st.mt = fmaxf(st.mt, row_max(scores(stage, ln, st, kb, key0, partial)));
   }
 };
 
@@ -410,10 +482,11 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
     }
   }
   st.m = -INFINITY;
+  st.neg_mc = 0.0f;
   st.mt = -INFINITY;
+  bool need_ref = true;
 
   const float c_log2 = a.scale * kLog2e;
-  const float tau_raw = kRefSlackLog2 / c_log2;
 
   auto dma = [&](char LDS_AS* stage, int kt, int kb) {
     const int key0 = kt * kBlockK + kb * kHalf;
@@ -432,15 +505,8 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
     }
   };
 
-  for (int pass = 0;; ++pass) {
-#pragma unroll
-    for (int i = 0; i < C::kOBlocks; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.o[i][r] = 0.0f;
-    st.l = 0.0f;
-    st.lb = 0.0f;
-    bool bad = false;
-
+  // Walks the kept tiles in 32-key halves, calling half(stage, key0, kb, partial).
+  auto walk = [&](auto&& half) {
     load_list(e_begin);
     if (e_begin < e_end) dma(smem, tile_of(e_begin), 0);
     int cur = 0;  // byte offset of the stage holding the current half
@@ -457,13 +523,39 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
           if (e + 1 - list_e0 == 64) load_list(e + 1);
           dma(smem + (cur ^ C::kStageBytes), tile_of(e + 1), 0);
         }
-        K::compute_half(smem + cur, ln, st, kb, kt * kBlockK, partial, c_log2, tau_raw, bad);
+        half(smem + cur, kt * kBlockK, kb, partial);
         cur ^= C::kStageBytes;
       }
     }
-    // second pass (rare): some row's max outgrew its reference; rerun with the exact maxima
-    if (pass == 1 || !__syncthreads_or(bad)) break;
+    __syncthreads();  // all reads of the last stage are done before another walk refills it
+  };
+  auto attend = [&](const char LDS_AS* stage, int key0, int kb, bool partial) {
+    K::compute_half(stage, ln, st, kb, key0, partial, c_log2, need_ref);
+  };
+  auto clear = [&]() {
+#pragma unroll
+    for (int i = 0; i < C::kOBlocks; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[i][r] = 0.0f;
+    st.l = 0.0f;
+    st.lb = 0.0f;
+  };
+
+  // Usual case: one walk with a fixed reference per row.  Every P of a row is
+  // at most its row sum, so below kSumLimit nothing lost range; otherwise
+  // walk again for the exact row maxima and once more with them as the
+  // reference (then every P <= 1).
+  clear();
+  walk(attend);
+  if (__syncthreads_or(!(st.l <= kSumLimit))) {
+    walk([&](const char LDS_AS* stage, int key0, int kb, bool partial) {
+      K::max_half(stage, ln, st, kb, key0, partial);
+    });
     st.m = st.mt;
+    st.neg_mc = st.mt == -INFINITY ? 0.0f : -st.mt * c_log2;
+    need_ref = false;
+    clear();
+    walk(attend);
   }
 
   // epilogue
