@@ -18,6 +18,10 @@ What it computes (all in float64, from the exact bf16 input values):
                    per row block over the gathered kept keys.
 * ``brute``     -- the same quantities with pure-Python loops and
                    ``math.fsum``, for tiny inputs only.
+* ``dynamic``   -- dynamic block-sparse tile selection for the dense layers
+                   (probe queries against pooled keys, max-based threshold;
+                   FlashPrefill page, sections 2.1-2.3) and attention over an
+                   explicit per-head tile list.
 
 Sources (the pages this method is described on):
   * "TriangleMix" blog post (PaperWeekly / news.fishai.com.cn), sections
@@ -27,8 +31,9 @@ Sources (the pages this method is described on):
     paragraphs: only the streaming region (the beginning part) and the final
     "Last Q-K" aggregation region are kept; complexity falls to O(N).
 
-Every function here is pinned by tests in ``tests/test_oracle_pins.py``
+Every function here is pinned by tests in ``tests/test_oracle_pins.py`` and
+``tests/test_oracle_dynamic.py``
 (brute force, closed forms, library attention on the special cases that
 reduce to it, and hand-derived tile grids); none is "parity unpinned".
 """
-from . import mask, attention, brute  # noqa: F401
+from . import mask, attention, brute, dynamic  # noqa: F401
