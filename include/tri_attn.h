@@ -136,6 +136,72 @@ int tri_attn_prefill(const tri_attn_tensors* t, const tri_mask_params* mp,
  */
 int dense_causal_prefill(const tri_attn_tensors* t, void* stream);
 
+/*
+ * Dynamic block-sparse lists for the dense (shallow) layers.
+ *
+ * The TriangleMix pages leave the shallow layers dense and note that a
+ * dynamic sparse method can be used there on top of the static triangle
+ * layers.  The FlashPrefill page gives such a method: evenly spread query
+ * rows act as probes (section 2.1), each key block is represented by the
+ * mean of its keys (2.1), a key block is kept when its score reaches alpha
+ * times the largest score of its query block, with no sort (2.2), and the
+ * kept blocks are walked through an index list (2.3).  Here the blocks are
+ * the kernel tiles (TRI_KERNEL_BLOCK_Q query rows x TRI_KERNEL_BLOCK_K keys):
+ *   - probes of query tile t: rows t*128 + 8p, p = 0..15, that are < N;
+ *   - kbar_kt: the mean of the keys of tile kt (keys < N), rounded to bf16;
+ *   - probe i sees the tiles kt with 64*kt <= i; its attention over them is
+ *     softmax_kt(softmax_scale * <q_i, kbar_kt>);
+ *   - score(t, kt): that attention averaged over the tile's probes;
+ *   - kt (0 <= 64*kt <= last row of t) is kept when score >= alpha * max
+ *     score, and always when it crosses the causal diagonal of the query
+ *     tile (64*kt + 63 > 128*t), so no row is ever empty.
+ * The result is a CSR list per (batch, query head): row r = (b*heads_q + h)
+ * * nq + t (nq = ceil(N/128)) spans d_k_tile[row_ptr[r] .. row_ptr[r+1]),
+ * ascending, with causal flags (TRI_TILE_FULL iff every key of the tile is
+ * <= the tile's first row).
+ */
+enum { TRI_DYN_PROBES = 16 };
+
+typedef struct {
+  float alpha;      /* keep threshold factor, 0 <= alpha <= 1 (0 keeps every causal tile) */
+  int32_t n_probe;  /* probe rows per query tile; must be TRI_DYN_PROBES */
+} tri_dyn_params;
+
+/*
+ * tri_dyn_plan_sizes -- host only.  For the layer described by *t (its q and
+ * k are what tri_dyn_plan reads; every field is validated as for the prefill
+ * calls), writes the device workspace size in bytes, the number of list rows
+ * (batch * heads_q * nq; row_ptr needs one more entry) and the largest
+ * possible number of list entries (every causal tile kept), which is the
+ * capacity tri_dyn_plan requires for d_k_tile and d_flags.
+ * Workspace layout (byte offsets from its start): bf16 pooled keys
+ * [batch, heads_kv, ceil(N/64), head_dim] at 0; the rest is scratch.
+ */
+int tri_dyn_plan_sizes(const tri_attn_tensors* t, int64_t* workspace_bytes, int64_t* n_rows,
+                       int64_t* max_nnz);
+
+/*
+ * tri_dyn_plan -- enqueue the selection on `stream` and return.  The caller
+ * owns the 256-byte-aligned device workspace (>= workspace_bytes of
+ * tri_dyn_plan_sizes) and the device outputs d_row_ptr [n_rows + 1],
+ * d_k_tile and d_flags [capacity >= max_nnz].  No host synchronisation: the
+ * list length is d_row_ptr[n_rows] on the device.
+ */
+int tri_dyn_plan(const tri_attn_tensors* t, const tri_dyn_params* dp, void* d_workspace,
+                 int64_t workspace_bytes, int32_t* d_row_ptr, int32_t* d_k_tile, uint8_t* d_flags,
+                 int64_t capacity, void* stream);
+
+/*
+ * tri_attn_prefill_lists -- the attention kernel walking per-(batch, head)
+ * tile lists in the format above (e.g. tri_dyn_plan's output), with the
+ * causal mask inside the listed tiles: row i keeps the keys of its query
+ * tile's listed key tiles that are <= i.  The lists must be ascending, hold
+ * only tiles kt with 64*kt <= the tile's last row, and include the tiles
+ * crossing the diagonal, flagged as above.
+ */
+int tri_attn_prefill_lists(const tri_attn_tensors* t, const int32_t* d_row_ptr,
+                           const int32_t* d_k_tile, const uint8_t* d_flags, void* stream);
+
 /* Message for the last non-OK return on this thread ("" if none). */
 const char* tri_attn_last_error(void);
 

@@ -19,14 +19,16 @@ import math
 from ._abi import (  # noqa: F401
     TRI_DTYPE_BF16, TRI_DTYPE_F32, TRI_ERR_CAPACITY, TRI_ERR_HIP, TRI_ERR_INVALID,
     TRI_ERR_UNSUPPORTED, TRI_KERNEL_BLOCK_K, TRI_KERNEL_BLOCK_Q, TRI_MASK_CAUSAL,
-    TRI_MASK_TRIANGLE, TRI_OK, TRI_TILE_FULL, TRI_TILE_PARTIAL, AttnTensors, MaskParams,
-    TriAttnError, dense_causal_prefill, last_error, load, mask_params, tri_attn_abi_version,
-    tri_attn_plan, tri_attn_prefill, tri_attn_work_item,
+    TRI_MASK_TRIANGLE, TRI_OK, TRI_TILE_FULL, TRI_TILE_PARTIAL, TRI_DYN_PROBES, AttnTensors,
+    DynParams, MaskParams, TriAttnError, dense_causal_prefill, last_error, load, mask_params,
+    tri_attn_abi_version, tri_attn_plan, tri_attn_prefill, tri_attn_prefill_lists,
+    tri_attn_work_item, tri_dyn_plan, tri_dyn_plan_sizes,
 )
 
 __all__ = [
     "prefill", "DevicePlan", "device_plan", "make_tensors", "tri_attn_plan", "tri_attn_prefill",
     "dense_causal_prefill", "mask_params", "TriAttnError", "last_error", "layer_mode",
+    "DynPlan", "dyn_plan", "tri_dyn_plan", "tri_dyn_plan_sizes", "tri_attn_prefill_lists",
 ]
 
 
@@ -98,10 +100,42 @@ def make_tensors(q, k, v, o, lse=None, scale=None) -> AttnTensors:
     return t
 
 
+class DynPlan:
+    """Device buffers of a dynamic block-sparse plan (tri_dyn_plan): workspace,
+    row_ptr [n_rows + 1], k_tile and flags [max_nnz], all torch tensors."""
+
+    def __init__(self, t: AttnTensors, device):
+        import torch
+        self.workspace_bytes, self.n_rows, self.max_nnz = tri_dyn_plan_sizes(t)
+        # torch's caching allocator returns 512-byte-aligned blocks
+        self.workspace = torch.empty(max(256, self.workspace_bytes), dtype=torch.uint8, device=device)
+        self.d_row_ptr = torch.empty(self.n_rows + 1, dtype=torch.int32, device=device)
+        self.d_k_tile = torch.empty(max(1, self.max_nnz), dtype=torch.int32, device=device)
+        self.d_flags = torch.empty(max(1, self.max_nnz), dtype=torch.uint8, device=device)
+
+    def run(self, t: AttnTensors, alpha: float, stream: int) -> None:
+        tri_dyn_plan(t, alpha, self.workspace.data_ptr(), self.workspace.numel(),
+                     self.d_row_ptr.data_ptr(), self.d_k_tile.data_ptr(), self.d_flags.data_ptr(),
+                     self.d_k_tile.numel(), stream)
+
+
+def dyn_plan(q, k, alpha, scale=None, stream=None) -> DynPlan:
+    """Dynamic tile lists of a dense layer (FlashPrefill-style probe selection)."""
+    import torch
+    # the selection reads q and k only; o is a placeholder the call never writes
+    o = torch.empty((1, 1, 1, 8), dtype=torch.bfloat16, device=q.device)
+    t = make_tensors(q, k, k, o, None, scale)
+    p = DynPlan(t, q.device)
+    s = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
+    p.run(t, alpha, s)
+    return p
+
+
 def prefill(q, k, v, mode="triangle", sink=0, window=1, last_q=0, o_dtype=None, scale=None,
-            out=None, lse=None, stream=None):
+            out=None, lse=None, stream=None, plan=None):
     """One attention layer on the GPU; returns (o, lse).  ``mode`` is
-    "triangle" (planned tile list) or "causal" (dense layer)."""
+    "triangle" (planned tile list), "causal" (dense layer) or "lists"
+    (per-head tile lists of a DynPlan, causal mask inside the tiles)."""
     import torch
     B, Hq, N, d = q.shape
     if o_dtype is None:
@@ -118,6 +152,11 @@ def prefill(q, k, v, mode="triangle", sink=0, window=1, last_q=0, o_dtype=None, 
         p = device_plan(N, "triangle", sink, window, last_q, q.device)
         tri_attn_prefill(t, p.mp, p.d_row_ptr.data_ptr(), p.d_k_tile.data_ptr(),
                          p.d_flags.data_ptr(), s)
+    elif mode == "lists":
+        if plan is None:
+            raise ValueError("mode 'lists' needs plan= (a DynPlan)")
+        tri_attn_prefill_lists(t, plan.d_row_ptr.data_ptr(), plan.d_k_tile.data_ptr(),
+                               plan.d_flags.data_ptr(), s)
     else:
         raise ValueError(f"unknown mode {mode!r}")
     return out, lse

@@ -28,6 +28,7 @@ TRI_TILE_FULL = 0
 TRI_TILE_PARTIAL = 1
 TRI_KERNEL_BLOCK_Q = 128
 TRI_KERNEL_BLOCK_K = 64
+TRI_DYN_PROBES = 16
 
 _STATUS_NAMES = {
     TRI_OK: "TRI_OK", TRI_ERR_INVALID: "TRI_ERR_INVALID", TRI_ERR_CAPACITY: "TRI_ERR_CAPACITY",
@@ -76,6 +77,13 @@ class AttnTensors(ctypes.Structure):
     ]
 
 
+class DynParams(ctypes.Structure):
+    _fields_ = [
+        ("alpha", ctypes.c_float),
+        ("n_probe", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -108,6 +116,16 @@ def load() -> ctypes.CDLL:
                                        ctypes.c_int64, P(ctypes.c_int32), P(ctypes.c_int32),
                                        P(ctypes.c_int32), P(ctypes.c_int64)]
     lib.tri_attn_work_item.restype = ctypes.c_int
+    lib.tri_dyn_plan_sizes.argtypes = [P(AttnTensors), P(ctypes.c_int64), P(ctypes.c_int64),
+                                       P(ctypes.c_int64)]
+    lib.tri_dyn_plan_sizes.restype = ctypes.c_int
+    lib.tri_dyn_plan.argtypes = [P(AttnTensors), P(DynParams), ctypes.c_void_p, ctypes.c_int64,
+                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                 ctypes.c_void_p]
+    lib.tri_dyn_plan.restype = ctypes.c_int
+    lib.tri_attn_prefill_lists.argtypes = [P(AttnTensors), ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+    lib.tri_attn_prefill_lists.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -174,3 +192,28 @@ def tri_attn_work_item(batch, heads_q, heads_kv, seqlen, kind, last_q, bid):
                                      ctypes.byref(b), ctypes.byref(h), ctypes.byref(t),
                                      ctypes.byref(grid)))
     return b.value, h.value, t.value, grid.value
+
+
+def tri_dyn_plan_sizes(t: AttnTensors):
+    """(workspace_bytes, n_rows, max_nnz) of the dynamic plan of layer ``t``."""
+    ws = ctypes.c_int64()
+    rows = ctypes.c_int64()
+    nnz = ctypes.c_int64()
+    _check(load().tri_dyn_plan_sizes(ctypes.byref(t), ctypes.byref(ws), ctypes.byref(rows),
+                                     ctypes.byref(nnz)))
+    return ws.value, rows.value, nnz.value
+
+
+def tri_dyn_plan(t: AttnTensors, alpha: float, d_workspace: int, workspace_bytes: int,
+                 d_row_ptr: int, d_k_tile: int, d_flags: int, capacity: int, stream: int,
+                 n_probe: int = TRI_DYN_PROBES) -> None:
+    """Enqueue the dynamic tile selection; pointers are device addresses."""
+    dp = DynParams(float(alpha), int(n_probe))
+    _check(load().tri_dyn_plan(ctypes.byref(t), ctypes.byref(dp), d_workspace, workspace_bytes,
+                               d_row_ptr, d_k_tile, d_flags, capacity, stream))
+
+
+def tri_attn_prefill_lists(t: AttnTensors, d_row_ptr: int, d_k_tile: int, d_flags: int,
+                           stream: int) -> None:
+    """Enqueue attention over per-(batch, head) tile lists."""
+    _check(load().tri_attn_prefill_lists(ctypes.byref(t), d_row_ptr, d_k_tile, d_flags, stream))

@@ -46,12 +46,14 @@ def build(verbose: bool = False, lib_path: str = LIB, kernel_src: str = None,
         obj = os.path.join(build_dir, src + ".o")
         _run(["g++", *HOST_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
-    kobj = os.path.join(build_dir, "attn_fwd_gfx950.o")
-    out = _run([hipcc, *HIPCC_FLAGS, *extra_hipcc_flags, "-I", INCLUDE, "-I", CSRC, "-c",
-                kernel_src or os.path.join(CSRC, "attn_fwd_gfx950.hip"), "-o", kobj])
-    if verbose and out.strip():
-        print(out)
-    objs.append(kobj)
+    for name, src in (("attn_fwd_gfx950", kernel_src or os.path.join(CSRC, "attn_fwd_gfx950.hip")),
+                      ("dyn_select_gfx950", os.path.join(CSRC, "dyn_select_gfx950.hip"))):
+        kobj = os.path.join(build_dir, name + ".o")
+        out = _run([hipcc, *HIPCC_FLAGS, *extra_hipcc_flags, "-I", INCLUDE, "-I", CSRC, "-c", src,
+                    "-o", kobj])
+        if verbose and out.strip():
+            print(out)
+        objs.append(kobj)
     tmp = lib_path + ".tmp"
     _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, lib_path)

@@ -113,14 +113,39 @@ AttnLaunch make_launch(const tri_attn_tensors* t, bool causal, int64_t sink, int
   return a;
 }
 
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// Largest list of a dense layer: every causal key tile of every query tile.
+int64_t causal_tiles(int64_t N) {
+  const int64_t nq = (N + TRI_KERNEL_BLOCK_Q - 1) / TRI_KERNEL_BLOCK_Q;
+  int64_t n = 0;
+  for (int64_t t = 0; t < nq; ++t)
+    n += (std::min(N, (t + 1) * TRI_KERNEL_BLOCK_Q) - 1) / TRI_KERNEL_BLOCK_K + 1;
+  return n;
+}
+
 }  // namespace
+
+DynWorkspace dyn_workspace(int64_t batch, int64_t heads_q, int64_t heads_kv, int64_t head_dim,
+                           int64_t seqlen) {
+  const int64_t nq = (seqlen + TRI_KERNEL_BLOCK_Q - 1) / TRI_KERNEL_BLOCK_Q;
+  const int64_t nkt = (seqlen + TRI_KERNEL_BLOCK_K - 1) / TRI_KERNEL_BLOCK_K;
+  const int64_t words = (nkt + 31) / 32;
+  DynWorkspace w{};
+  w.pooled = 0;
+  w.bitmap = align256(batch * heads_kv * nkt * head_dim * 2);
+  w.counts = w.bitmap + align256(batch * heads_q * nq * words * 4);
+  w.total = w.counts + align256(batch * heads_q * nq * 4);
+  return w;
+}
+
 }  // namespace triattn
 
 using namespace triattn;
 
 extern "C" const char* tri_attn_last_error(void) { return g_error; }
 
-extern "C" int tri_attn_abi_version(void) { return 1; }
+extern "C" int tri_attn_abi_version(void) { return 2; }
 
 extern "C" int tri_attn_prefill(const tri_attn_tensors* t, const tri_mask_params* mp,
                                 const int32_t* d_row_ptr, const int32_t* d_k_tile,
@@ -184,4 +209,100 @@ extern "C" int tri_attn_work_item(int32_t batch, int32_t heads_q, int32_t heads_
   *qtile_out = w.t;
   *grid_out = s.grid;
   return TRI_OK;
+}
+
+extern "C" int tri_dyn_plan_sizes(const tri_attn_tensors* t, int64_t* workspace_bytes,
+                                  int64_t* n_rows, int64_t* max_nnz) {
+  clear_error();
+  int st = validate_tensors(t);
+  if (st != TRI_OK) return st;
+  if (!workspace_bytes || !n_rows || !max_nnz)
+    return fail(TRI_ERR_INVALID, "output pointers must be non-NULL");
+  const int64_t nq = (t->seqlen + TRI_KERNEL_BLOCK_Q - 1) / TRI_KERNEL_BLOCK_Q;
+  *workspace_bytes = dyn_workspace(t->batch, t->heads_q, t->heads_kv, t->head_dim, t->seqlen).total;
+  *n_rows = static_cast<int64_t>(t->batch) * t->heads_q * nq;
+  *max_nnz = static_cast<int64_t>(t->batch) * t->heads_q * causal_tiles(t->seqlen);
+  return TRI_OK;
+}
+
+extern "C" int tri_dyn_plan(const tri_attn_tensors* t, const tri_dyn_params* dp, void* d_workspace,
+                            int64_t workspace_bytes, int32_t* d_row_ptr, int32_t* d_k_tile,
+                            uint8_t* d_flags, int64_t capacity, void* stream) {
+  clear_error();
+  int st = validate_tensors(t);
+  if (st != TRI_OK) return st;
+  if (!dp) return fail(TRI_ERR_INVALID, "dynamic-plan parameters pointer is NULL");
+  if (!(dp->alpha >= 0.0f && dp->alpha <= 1.0f))
+    return fail(TRI_ERR_INVALID, "alpha must be in [0, 1]");
+  if (dp->n_probe != TRI_DYN_PROBES)
+    return fail(TRI_ERR_UNSUPPORTED, "n_probe must be %d", TRI_DYN_PROBES);
+  const int64_t N = t->seqlen;
+  const int64_t nq = (N + TRI_KERNEL_BLOCK_Q - 1) / TRI_KERNEL_BLOCK_Q;
+  const int64_t nkt = (N + TRI_KERNEL_BLOCK_K - 1) / TRI_KERNEL_BLOCK_K;
+  const int64_t rows = static_cast<int64_t>(t->batch) * t->heads_q * nq;
+  const int64_t need = static_cast<int64_t>(t->batch) * t->heads_q * causal_tiles(N);
+  const DynWorkspace ws = dyn_workspace(t->batch, t->heads_q, t->heads_kv, t->head_dim, N);
+  if (need >= INT32_MAX || rows >= INT32_MAX)
+    return fail(TRI_ERR_UNSUPPORTED, "list sizes exceed 2^31-1 entries");
+  if (!d_workspace || !d_row_ptr || !d_k_tile || !d_flags)
+    return fail(TRI_ERR_INVALID, "workspace and output pointers must be non-NULL");
+  if (!aligned(d_workspace, 256)) return fail(TRI_ERR_INVALID, "workspace must be 256-byte aligned");
+  if (!aligned(d_row_ptr, 4) || !aligned(d_k_tile, 4))
+    return fail(TRI_ERR_INVALID, "row_ptr and k_tile must be 4-byte aligned");
+  if (workspace_bytes < ws.total)
+    return fail(TRI_ERR_CAPACITY, "workspace of %lld bytes, %lld needed",
+                static_cast<long long>(workspace_bytes), static_cast<long long>(ws.total));
+  if (capacity < need)
+    return fail(TRI_ERR_CAPACITY, "list capacity %lld, %lld needed", static_cast<long long>(capacity),
+                static_cast<long long>(need));
+  if (N == 0) return TRI_OK;
+  DynLaunch a{};
+  a.q = t->q;
+  a.k = t->k;
+  memcpy(a.q_stride, t->q_stride, sizeof(a.q_stride));
+  memcpy(a.k_stride, t->k_stride, sizeof(a.k_stride));
+  a.batch = t->batch;
+  a.heads_q = t->heads_q;
+  a.heads_kv = t->heads_kv;
+  a.head_dim = t->head_dim;
+  a.seqlen = static_cast<int32_t>(N);
+  a.nq = static_cast<int32_t>(nq);
+  a.nkt = static_cast<int32_t>(nkt);
+  a.words = static_cast<int32_t>((nkt + 31) / 32);
+  a.n_rows = rows;
+  a.n_pool_tiles = static_cast<int64_t>(t->batch) * t->heads_kv * nkt;
+  a.scale = t->softmax_scale;
+  a.alpha = dp->alpha;
+  char* w = static_cast<char*>(d_workspace);
+  a.pooled = w + ws.pooled;
+  a.bitmap = reinterpret_cast<uint32_t*>(w + ws.bitmap);
+  a.counts = reinterpret_cast<int32_t*>(w + ws.counts);
+  a.row_ptr = d_row_ptr;
+  a.k_tile = d_k_tile;
+  a.flags = d_flags;
+  return launch_dyn_plan(a, stream);
+}
+
+extern "C" int tri_attn_prefill_lists(const tri_attn_tensors* t, const int32_t* d_row_ptr,
+                                      const int32_t* d_k_tile, const uint8_t* d_flags,
+                                      void* stream) {
+  clear_error();
+  int st = validate_tensors(t);
+  if (st != TRI_OK) return st;
+  if (!d_row_ptr || !d_k_tile || !d_flags)
+    return fail(TRI_ERR_INVALID, "list arrays (row_ptr, k_tile, flags) must be non-NULL");
+  if (!aligned(d_row_ptr, 4) || !aligned(d_k_tile, 4))
+    return fail(TRI_ERR_INVALID, "row_ptr and k_tile must be 4-byte aligned");
+  const int64_t nq = (t->seqlen + TRI_KERNEL_BLOCK_Q - 1) / TRI_KERNEL_BLOCK_Q;
+  if (static_cast<int64_t>(t->batch) * t->heads_q * nq >= INT32_MAX)
+    return fail(TRI_ERR_UNSUPPORTED, "list rows exceed 2^31-1");
+  if (t->seqlen == 0) return TRI_OK;
+  // causal schedule (longest lists first) and causal mask inside the listed tiles
+  AttnLaunch a = make_launch(t, true, 0, 1, t->seqlen);
+  a.causal = 0;
+  a.row_ptr = d_row_ptr;
+  a.k_tile = d_k_tile;
+  a.flags = d_flags;
+  a.list_rows_per_head = static_cast<int32_t>(nq);
+  return launch_attn_fwd(a, stream);
 }

@@ -444,8 +444,11 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
     e_begin = 0;
     e_end = (min(N, q0 + kBlockQ) - 1) / kBlockK + 1;
   } else {
-    e_begin = a.row_ptr[w.t];
-    e_end = a.row_ptr[w.t + 1];
+    const int64_t r = a.list_rows_per_head == 0
+                          ? w.t
+                          : (static_cast<int64_t>(w.b) * a.sched.heads_q + w.h) * a.list_rows_per_head + w.t;
+    e_begin = a.row_ptr[r];
+    e_end = a.row_ptr[r + 1];
   }
   // tile list in registers, 64 entries per batch (lane i holds entry e0 + i)
   int list_e0 = e_begin;

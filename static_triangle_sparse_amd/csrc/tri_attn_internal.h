@@ -131,10 +131,43 @@ struct AttnLaunch {
   const int32_t* row_ptr;
   const int32_t* k_tile;
   const uint8_t* flags;
+  // 0: one list shared by every (batch, head), row t; n > 0: per-head lists,
+  // row (b * heads_q + h) * n + t (n = query tiles)
+  int32_t list_rows_per_head;
   Schedule sched;
 };
 
 // Enqueue the gfx950 kernel; returns TRI_OK or TRI_ERR_HIP.
 int launch_attn_fwd(const AttnLaunch& a, void* stream);
+
+// ---------------------------------------------------------------- dynamic plan
+
+struct DynLaunch {
+  const void* q;  // bf16 [B, Hq, N, d]
+  const void* k;  // bf16 [B, Hkv, N, d]
+  int64_t q_stride[3], k_stride[3];
+  int32_t batch, heads_q, heads_kv, head_dim, seqlen;
+  int32_t nq, nkt;       // query tiles, key tiles
+  int32_t words;         // keep-bitmap words per row: ceil(nkt / 32)
+  int64_t n_rows;        // batch * heads_q * nq
+  int64_t n_pool_tiles;  // batch * heads_kv * nkt
+  float scale, alpha;
+  void* pooled;       // workspace: bf16 [B, Hkv, nkt, d]
+  uint32_t* bitmap;   // workspace: [n_rows, words]
+  int32_t* counts;    // workspace: [n_rows]
+  int32_t* row_ptr;   // out: [n_rows + 1]
+  int32_t* k_tile;    // out
+  uint8_t* flags;     // out
+};
+
+// Workspace layout of the dynamic plan (byte offsets, each 256-aligned).
+struct DynWorkspace {
+  int64_t pooled, bitmap, counts, total;
+};
+DynWorkspace dyn_workspace(int64_t batch, int64_t heads_q, int64_t heads_kv, int64_t head_dim,
+                           int64_t seqlen);
+
+// Enqueue the four launches of the dynamic plan; returns TRI_OK or TRI_ERR_HIP.
+int launch_dyn_plan(const DynLaunch& a, void* stream);
 
 }  // namespace triattn

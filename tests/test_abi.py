@@ -23,11 +23,12 @@ def _declared_functions():
 def test_header_symbols_are_exported():
     names = _declared_functions()
     assert {"tri_attn_plan", "tri_attn_prefill", "dense_causal_prefill",
-            "tri_attn_last_error"} <= set(names)
+            "tri_attn_last_error", "tri_dyn_plan_sizes", "tri_dyn_plan",
+            "tri_attn_prefill_lists"} <= set(names)
     lib = ctypes.CDLL(_abi.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert tsa.tri_attn_abi_version() == 1
+    assert tsa.tri_attn_abi_version() == 2
 
 
 # ----------------------------------------------------------- plan validation
@@ -158,6 +159,70 @@ def test_empty_sequence_is_a_no_op():
     mp = tsa.mask_params(0, "triangle", 4, 64, 16)
     P = 1 << 24
     assert _abi.load().tri_attn_prefill(ctypes.byref(t), ctypes.byref(mp), P, P, P, None) == tsa.TRI_OK
+
+
+# ------------------------------------------------------------ dynamic plan
+
+def _causal_tiles(N):
+    return sum((min(N, (t + 1) * 128) - 1) // 64 + 1 for t in range(-(-N // 128)))
+
+
+def test_dyn_plan_sizes():
+    for B, Hq, Hkv, N, d in [(1, 4, 2, 256, 128), (2, 28, 4, 1000, 64), (1, 32, 8, 131072, 128),
+                             (1, 1, 1, 1, 64)]:
+        t = _good_tensors(B, Hq, Hkv, N, d)
+        ws, rows, nnz = tsa.tri_dyn_plan_sizes(t)
+        nq, nkt = -(-N // 128), -(-N // 64)
+        assert rows == B * Hq * nq
+        assert nnz == B * Hq * _causal_tiles(N)
+        pooled = -(-(B * Hkv * nkt * d * 2) // 256) * 256
+        assert ws >= pooled + B * Hq * nq * (4 * -(-nkt // 32) + 4)
+        assert ws % 256 == 0
+    assert _causal_tiles(131072) == 1049600  # the dense 128K layer's tile count
+
+
+def test_dyn_plan_rejects_bad_arguments():
+    lib = _abi.load()
+    t = _good_tensors(N=1000)
+    ws, rows, nnz = tsa.tri_dyn_plan_sizes(t)
+    W = 1 << 26  # fake, 256-byte-aligned device addresses: never dereferenced
+    P = 1 << 27
+
+    def call(alpha=0.5, n_probe=16, w=W, wbytes=ws, rp=P, kt=P, fl=P, cap=nnz, tt=t):
+        dp = tsa.DynParams(alpha, n_probe)
+        return lib.tri_dyn_plan(ctypes.byref(tt) if tt is not None else None, ctypes.byref(dp),
+                                w, wbytes, rp, kt, fl, cap, None)
+
+    assert call(tt=None) == tsa.TRI_ERR_INVALID
+    assert lib.tri_dyn_plan(ctypes.byref(t), None, W, ws, P, P, P, nnz, None) == tsa.TRI_ERR_INVALID
+    for a in (-0.1, 1.5, float("nan")):
+        assert call(alpha=a) == tsa.TRI_ERR_INVALID
+    assert call(n_probe=8) == tsa.TRI_ERR_UNSUPPORTED
+    assert call(w=None) == tsa.TRI_ERR_INVALID
+    assert call(w=W + 128) == tsa.TRI_ERR_INVALID
+    assert call(rp=None) == tsa.TRI_ERR_INVALID
+    assert call(kt=P + 2) == tsa.TRI_ERR_INVALID
+    assert call(wbytes=ws - 1) == tsa.TRI_ERR_CAPACITY
+    assert call(cap=nnz - 1) == tsa.TRI_ERR_CAPACITY
+    assert "capacity" in tsa.last_error()
+    bad = _good_tensors(N=1000, d=96)
+    assert call(tt=bad) == tsa.TRI_ERR_UNSUPPORTED
+    # N == 0 validates and returns before any HIP call
+    z = _good_tensors(N=0)
+    ws0, _, nnz0 = tsa.tri_dyn_plan_sizes(z)
+    assert call(tt=z, wbytes=ws0, cap=nnz0) == tsa.TRI_OK
+
+
+def test_prefill_lists_rejects_bad_arguments():
+    lib = _abi.load()
+    t = _good_tensors()
+    P = 1 << 24
+    assert lib.tri_attn_prefill_lists(None, P, P, P, None) == tsa.TRI_ERR_INVALID
+    assert lib.tri_attn_prefill_lists(ctypes.byref(t), None, P, P, None) == tsa.TRI_ERR_INVALID
+    assert lib.tri_attn_prefill_lists(ctypes.byref(t), P, None, P, None) == tsa.TRI_ERR_INVALID
+    assert lib.tri_attn_prefill_lists(ctypes.byref(t), P, P, None, None) == tsa.TRI_ERR_INVALID
+    assert lib.tri_attn_prefill_lists(ctypes.byref(t), P + 1, P, P, None) == tsa.TRI_ERR_INVALID
+    assert lib.tri_attn_prefill_lists(ctypes.byref(_good_tensors(N=0)), P, P, P, None) == tsa.TRI_OK
 
 
 # ----------------------------------------------------------------- schedule
