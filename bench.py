@@ -169,6 +169,28 @@ def cpu_baseline(bits, cfg, plan, n_random_tiles=128):
     }
 
 
+def bench_dynamic(t, args, dense_ms, d, Hq, B, dev, stream):
+    """The dense layer with dynamic block-sparse tile lists (probe queries
+    against pooled keys, keep at alpha x max; FlashPrefill page 2.1-2.3):
+    plan and list attention timed separately on the same inputs."""
+    import static_triangle_sparse_amd as tsa
+    plan = tsa.DynPlan(t, dev)
+    plan_ms, _ = time_launches(lambda: plan.run(t, args.dyn_alpha, stream), args.dense_steps, 1)
+    lists = lambda: tsa.tri_attn_prefill_lists(t, plan.d_row_ptr.data_ptr(), plan.d_k_tile.data_ptr(),
+                                               plan.d_flags.data_ptr(), stream)
+    attn_ms, _ = time_launches(lists, args.dense_steps, 1)
+    nnz = int(plan.d_row_ptr[-1].item())
+    kept_flops = 4.0 * 128 * 64 * d * nnz  # nnz already counts every (batch, head)
+    total = plan_ms + attn_ms
+    print(f"[bench] dynamic dense (alpha {args.dyn_alpha}): plan {plan_ms:.3f} ms + attention "
+          f"{attn_ms:.3f} ms, density {nnz / plan.max_nnz:.4f}", file=sys.stderr, flush=True)
+    return {"alpha": args.dyn_alpha, "plan_ms": round(plan_ms, 4), "attention_ms": round(attn_ms, 4),
+            "total_ms": round(total, 4), "density": round(nnz / plan.max_nnz, 4),
+            "kept_tflops": round(kept_flops / (attn_ms * 1e-3) / 1e12, 2),
+            "speedup_vs_dense": round(dense_ms / total, 2),
+            "inputs": "the same random N(0,1) tensors (near-uniform attention: density is high)"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +199,8 @@ def main(argv=None):
     ap.add_argument("--config", type=int, default=3, choices=sorted(CONFIGS))
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--dyn-alpha", type=float, default=0.9,
+                    help="keep threshold of the dynamic block-sparse dense layer (0 disables it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
@@ -227,6 +251,8 @@ def main(argv=None):
                  "triangle_speedup_vs_dense": round(dense_ms / tri_ms, 2),
                  "dense_kept_tiles_per_head": ctiles}
         print(f"[bench] dense causal: {dense_ms:.3f} ms/layer", file=sys.stderr, flush=True)
+        if args.dyn_alpha > 0:
+            extra["dynamic_dense"] = bench_dynamic(t, args, dense_ms, d, Hq, B, dev, stream)
 
     if args.calib_copy_mib:
         nbytes = args.calib_copy_mib << 20

@@ -11,8 +11,7 @@
 // Per 32-key half:
 //   1. K and V are copied HBM -> LDS by the LDS-DMA path (each lane's 16
 //      bytes land at LDS base + 16 * lane), double-buffered, one half ahead of
-//      the compute (the sparse kernel overlaps the copy with the compute; the
-//      dense causal kernel lets it finish first), without staging registers.
+//      the compute and overlapped with it, without staging registers.
 //      Rows are padded (K by 16 bytes, V by 64 bytes) so the MFMA operand
 //      reads below hit distinct LDS banks while every read address is a
 //      per-lane base plus a compile-time offset;
@@ -228,31 +227,6 @@ struct Kernel {
       const int blk = i * kWaves + wave;
       if (C::kVBlocks % kWaves == 0 || blk < C::kVBlocks)
         lds_dma16(v_rsrc, ln.v_dma[i], stage + C::kKBytes + blk * 1024);
-    }
-  }
-
-  // The same copies through the compiler's LDS-DMA builtin.  The compiler
-  // then makes the next LDS reads wait for every copy in flight, so the copy
-  // of the next half no longer overlaps the compute of this one.  The dense
-  // causal kernel walks contiguous key tiles whose copies hit in L2, and there
-  // this form measured faster (about 9% at 128K) than the overlapped one;
-  // the sparse kernel, whose kept tiles are scattered, is faster overlapped.
-  static __device__ __forceinline__ void issue_dma_builtin(char LDS_AS* stage, const Lane& ln, int wave,
-                                                           __amdgpu_buffer_rsrc_t k_rsrc,
-                                                           __amdgpu_buffer_rsrc_t v_rsrc) {
-#pragma unroll
-    for (int i = 0; i < C::kKBlocksPerWave; ++i) {
-      const int blk = i * kWaves + wave;
-      if (C::kKBlocks % kWaves == 0 || blk < C::kKBlocks)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (LDS_AS void*)(stage + blk * 1024), 16,
-                                                 static_cast<int>(ln.k_dma[i]), 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < C::kVBlocksPerWave; ++i) {
-      const int blk = i * kWaves + wave;
-      if (C::kVBlocks % kWaves == 0 || blk < C::kVBlocks)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (LDS_AS void*)(stage + C::kKBytes + blk * 1024),
-                                                 16, static_cast<int>(ln.v_dma[i]), 0, 0, 0);
     }
   }
 
@@ -496,16 +470,8 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
     // keys past the sequence end (the second half of a last tile can start
     // there) are outside the descriptor and land as zeros
     const int rows = max(N - key0, 0);
-    if constexpr (kCausal) {
-      const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(kbase + key0 * ks_b), 0, static_cast<int>(rows * ks_b), static_cast<int>(kRsrcWord3));
-      const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(vbase + key0 * vs_b), 0, static_cast<int>(rows * vs_b), static_cast<int>(kRsrcWord3));
-      K::issue_dma_builtin(stage, ln, wave, kr, vr);
-    } else {
-      K::issue_dma(stage, ln, wave, buffer_rsrc(kbase + key0 * ks_b, static_cast<uint32_t>(rows * ks_b)),
-                   buffer_rsrc(vbase + key0 * vs_b, static_cast<uint32_t>(rows * vs_b)));
-    }
+    K::issue_dma(stage, ln, wave, buffer_rsrc(kbase + key0 * ks_b, static_cast<uint32_t>(rows * ks_b)),
+                 buffer_rsrc(vbase + key0 * vs_b, static_cast<uint32_t>(rows * vs_b)));
   };
 
   // Walks the kept tiles in 32-key halves, calling half(stage, key0, kb, partial).
