@@ -191,6 +191,26 @@ def bench_dynamic(t, args, dense_ms, d, Hq, B, dev, stream):
             "inputs": "the same random N(0,1) tensors (near-uniform attention: density is high)"}
 
 
+def bench_per_head(t, args, cfg, d, Hq, B, dev, stream):
+    """The triangle layer with per-head boundaries (TriAttention page: each
+    head's region as diagonal-distance boundaries): windows 512, 1024, 2048,
+    4096 and sinks 0 / 128 cycling over the heads, last-Q as configured."""
+    import static_triangle_sparse_amd as tsa
+    window = [512 << (h % 4) for h in range(Hq)]
+    sink = [128 * (h % 2) for h in range(Hq)]
+    plan = tsa.head_plan(cfg["N"], sink, window, cfg["last_q"], dev)
+    run = lambda: tsa.tri_attn_prefill_heads(t, plan.mp, plan.d_sink.data_ptr(), plan.d_window.data_ptr(),
+                                             plan.d_row_ptr.data_ptr(), plan.d_k_tile.data_ptr(),
+                                             plan.d_flags.data_ptr(), stream)
+    ms, _ = time_launches(run, args.steps, args.warmup)
+    flops = 4.0 * 128 * 64 * d * plan.k_tile.size * B  # the plan lists every head
+    tf = flops / (ms * 1e-3) / 1e12
+    print(f"[bench] per-head triangle: {ms:.3f} ms/layer, {tf:.0f} TFLOP/s", file=sys.stderr, flush=True)
+    return {"windows": "512,1024,2048,4096 cycling", "sinks": "0,128 cycling", "ms": round(ms, 4),
+            "kept_tiles": int(plan.k_tile.size), "tflops": round(tf, 2),
+            "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,6 +219,8 @@ def main(argv=None):
     ap.add_argument("--config", type=int, default=3, choices=sorted(CONFIGS))
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--per-head", type=int, default=1,
+                    help="also time the triangle layer with per-head windows (0: skip)")
     ap.add_argument("--dyn-alpha", type=float, default=0.9,
                     help="keep threshold of the dynamic block-sparse dense layer (0 disables it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -253,6 +275,8 @@ def main(argv=None):
         print(f"[bench] dense causal: {dense_ms:.3f} ms/layer", file=sys.stderr, flush=True)
         if args.dyn_alpha > 0:
             extra["dynamic_dense"] = bench_dynamic(t, args, dense_ms, d, Hq, B, dev, stream)
+        if args.per_head:
+            extra["per_head_triangle"] = bench_per_head(t, args, cfg, d, Hq, B, dev, stream)
 
     if args.calib_copy_mib:
         nbytes = args.calib_copy_mib << 20

@@ -202,6 +202,37 @@ int tri_dyn_plan(const tri_attn_tensors* t, const tri_dyn_params* dp, void* d_wo
 int tri_attn_prefill_lists(const tri_attn_tensors* t, const int32_t* d_row_ptr,
                            const int32_t* d_k_tile, const uint8_t* d_flags, void* stream);
 
+/*
+ * Per-head boundaries of the triangle mask.  The TriAttention page encodes
+ * each attention head's computation region with two diagonal-distance
+ * boundaries, so that the policy's storage does not grow with the context.
+ * In the TriangleMix pattern the two per-head quantities are the sink length
+ * and the window (the diagonal distance below which keys are kept): head h
+ * keeps, for row i, the keys j <= i with j < sink[h], i - j < window[h], or
+ * i >= N - last_q (last_q stays one value for the layer).
+ *
+ * tri_attn_plan_heads -- host only, like tri_attn_plan; mp gives seqlen,
+ * tile shape, kind (must be TRI_MASK_TRIANGLE) and last_q (its sink and
+ * window are not used).  sink[heads], window[heads] (>= 0, >= 1; int32
+ * range).  Lists are CSR over rows h * n_qtiles + t (row_ptr has
+ * heads * n_qtiles + 1 entries), each list as tri_attn_plan would give for
+ * that head's (sink, window).  Sizing and capacity as in tri_attn_plan.
+ */
+int tri_attn_plan_heads(const tri_mask_params* mp, int32_t heads, const int64_t* sink,
+                        const int64_t* window, int32_t* row_ptr, int32_t* k_tile, uint8_t* flags,
+                        int64_t capacity, int32_t* n_qtiles_out, int64_t* nnz_out);
+
+/*
+ * tri_attn_prefill_heads -- a triangle layer with per-head boundaries: the
+ * device copy of tri_attn_plan_heads's output for heads = t->heads_q (shared
+ * by every batch entry) and device int32 arrays d_head_sink, d_head_window
+ * [heads_q] holding the same boundaries (values past N mean "everything").
+ */
+int tri_attn_prefill_heads(const tri_attn_tensors* t, const tri_mask_params* mp,
+                           const int32_t* d_head_sink, const int32_t* d_head_window,
+                           const int32_t* d_row_ptr, const int32_t* d_k_tile,
+                           const uint8_t* d_flags, void* stream);
+
 /* Message for the last non-OK return on this thread ("" if none). */
 const char* tri_attn_last_error(void);
 

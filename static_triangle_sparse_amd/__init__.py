@@ -16,19 +16,23 @@ from __future__ import annotations
 
 import math
 
+import numpy as np
+
 from ._abi import (  # noqa: F401
     TRI_DTYPE_BF16, TRI_DTYPE_F32, TRI_ERR_CAPACITY, TRI_ERR_HIP, TRI_ERR_INVALID,
     TRI_ERR_UNSUPPORTED, TRI_KERNEL_BLOCK_K, TRI_KERNEL_BLOCK_Q, TRI_MASK_CAUSAL,
     TRI_MASK_TRIANGLE, TRI_OK, TRI_TILE_FULL, TRI_TILE_PARTIAL, TRI_DYN_PROBES, AttnTensors,
     DynParams, MaskParams, TriAttnError, dense_causal_prefill, last_error, load, mask_params,
-    tri_attn_abi_version, tri_attn_plan, tri_attn_prefill, tri_attn_prefill_lists,
-    tri_attn_work_item, tri_dyn_plan, tri_dyn_plan_sizes,
+    tri_attn_abi_version, tri_attn_plan, tri_attn_plan_heads, tri_attn_prefill,
+    tri_attn_prefill_heads, tri_attn_prefill_lists, tri_attn_work_item, tri_dyn_plan,
+    tri_dyn_plan_sizes,
 )
 
 __all__ = [
     "prefill", "DevicePlan", "device_plan", "make_tensors", "tri_attn_plan", "tri_attn_prefill",
     "dense_causal_prefill", "mask_params", "TriAttnError", "last_error", "layer_mode",
     "DynPlan", "dyn_plan", "tri_dyn_plan", "tri_dyn_plan_sizes", "tri_attn_prefill_lists",
+    "HeadPlan", "head_plan", "tri_attn_plan_heads", "tri_attn_prefill_heads",
 ]
 
 
@@ -100,6 +104,33 @@ def make_tensors(q, k, v, o, lse=None, scale=None) -> AttnTensors:
     return t
 
 
+class HeadPlan:
+    """Per-head triangle plan (host numpy + device tensors) and the device
+    per-head boundary arrays."""
+
+    def __init__(self, seqlen, sink, window, last_q, device):
+        import torch
+        self.mp = mask_params(seqlen, "triangle", 0, 1, last_q)
+        self.sink = np.asarray(sink, dtype=np.int64)
+        self.window = np.asarray(window, dtype=np.int64)
+        self.row_ptr, self.k_tile, self.flags = tri_attn_plan_heads(self.mp, self.sink, self.window)
+        self.d_row_ptr = torch.from_numpy(self.row_ptr).to(device)
+        n = max(1, self.k_tile.size)
+        self.d_k_tile = torch.zeros(n, dtype=torch.int32, device=device)
+        self.d_flags = torch.zeros(n, dtype=torch.uint8, device=device)
+        if self.k_tile.size:
+            self.d_k_tile.copy_(torch.from_numpy(self.k_tile))
+            self.d_flags.copy_(torch.from_numpy(self.flags))
+        clip = lambda x: np.minimum(x, np.iinfo(np.int32).max).astype(np.int32)
+        self.d_sink = torch.from_numpy(clip(self.sink)).to(device)
+        self.d_window = torch.from_numpy(clip(self.window)).to(device)
+
+
+def head_plan(seqlen, sink, window, last_q=0, device="cuda") -> HeadPlan:
+    """Triangle plan with per-head sink and window (one value per query head)."""
+    return HeadPlan(seqlen, sink, window, last_q, device)
+
+
 class DynPlan:
     """Device buffers of a dynamic block-sparse plan (tri_dyn_plan): workspace,
     row_ptr [n_rows + 1], k_tile and flags [max_nnz], all torch tensors."""
@@ -152,6 +183,12 @@ def prefill(q, k, v, mode="triangle", sink=0, window=1, last_q=0, o_dtype=None, 
         p = device_plan(N, "triangle", sink, window, last_q, q.device)
         tri_attn_prefill(t, p.mp, p.d_row_ptr.data_ptr(), p.d_k_tile.data_ptr(),
                          p.d_flags.data_ptr(), s)
+    elif mode == "triangle_heads":
+        if plan is None:
+            raise ValueError("mode 'triangle_heads' needs plan= (a HeadPlan)")
+        tri_attn_prefill_heads(t, plan.mp, plan.d_sink.data_ptr(), plan.d_window.data_ptr(),
+                               plan.d_row_ptr.data_ptr(), plan.d_k_tile.data_ptr(),
+                               plan.d_flags.data_ptr(), s)
     elif mode == "lists":
         if plan is None:
             raise ValueError("mode 'lists' needs plan= (a DynPlan)")

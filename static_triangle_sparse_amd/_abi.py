@@ -126,6 +126,15 @@ def load() -> ctypes.CDLL:
     lib.tri_attn_prefill_lists.argtypes = [P(AttnTensors), ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_void_p]
     lib.tri_attn_prefill_lists.restype = ctypes.c_int
+    lib.tri_attn_plan_heads.argtypes = [P(MaskParams), ctypes.c_int32, P(ctypes.c_int64),
+                                        P(ctypes.c_int64), P(ctypes.c_int32), P(ctypes.c_int32),
+                                        P(ctypes.c_uint8), ctypes.c_int64, P(ctypes.c_int32),
+                                        P(ctypes.c_int64)]
+    lib.tri_attn_plan_heads.restype = ctypes.c_int
+    lib.tri_attn_prefill_heads.argtypes = [P(AttnTensors), P(MaskParams), ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+    lib.tri_attn_prefill_heads.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -217,3 +226,37 @@ def tri_attn_prefill_lists(t: AttnTensors, d_row_ptr: int, d_k_tile: int, d_flag
                            stream: int) -> None:
     """Enqueue attention over per-(batch, head) tile lists."""
     _check(load().tri_attn_prefill_lists(ctypes.byref(t), d_row_ptr, d_k_tile, d_flags, stream))
+
+
+def tri_attn_plan_heads(mp: MaskParams, sink, window):
+    """Host planner with per-head (sink, window).  Returns (row_ptr
+    int32[H*nq+1], k_tile int32[nnz], flags uint8[nnz]) over rows h*nq + t."""
+    lib = load()
+    sink = np.ascontiguousarray(sink, dtype=np.int64)
+    window = np.ascontiguousarray(window, dtype=np.int64)
+    if sink.shape != window.shape or sink.ndim != 1:
+        raise ValueError("sink and window must be 1-D of the same length")
+    H = sink.size
+    P64 = ctypes.POINTER(ctypes.c_int64)
+    nq = ctypes.c_int32()
+    nnz = ctypes.c_int64()
+    _check(lib.tri_attn_plan_heads(ctypes.byref(mp), H, sink.ctypes.data_as(P64),
+                                   window.ctypes.data_as(P64), None, None, None, 0,
+                                   ctypes.byref(nq), ctypes.byref(nnz)))
+    row_ptr = np.zeros(H * nq.value + 1, dtype=np.int32)
+    k_tile = np.zeros(max(1, nnz.value), dtype=np.int32)
+    flags = np.zeros(max(1, nnz.value), dtype=np.uint8)
+    _check(lib.tri_attn_plan_heads(
+        ctypes.byref(mp), H, sink.ctypes.data_as(P64), window.ctypes.data_as(P64),
+        row_ptr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+        k_tile.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+        flags.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), nnz.value, ctypes.byref(nq),
+        ctypes.byref(nnz)))
+    return row_ptr, k_tile[:nnz.value], flags[:nnz.value]
+
+
+def tri_attn_prefill_heads(t: AttnTensors, mp: MaskParams, d_head_sink: int, d_head_window: int,
+                           d_row_ptr: int, d_k_tile: int, d_flags: int, stream: int) -> None:
+    """Enqueue a triangle layer with per-head boundaries (device pointers)."""
+    _check(load().tri_attn_prefill_heads(ctypes.byref(t), ctypes.byref(mp), d_head_sink,
+                                         d_head_window, d_row_ptr, d_k_tile, d_flags, stream))

@@ -303,6 +303,41 @@ extern "C" int tri_attn_prefill_lists(const tri_attn_tensors* t, const int32_t* 
   a.row_ptr = d_row_ptr;
   a.k_tile = d_k_tile;
   a.flags = d_flags;
-  a.list_rows_per_head = static_cast<int32_t>(nq);
+  a.list_batch_rows = t->heads_q * nq;
+  a.list_head_rows = static_cast<int32_t>(nq);
+  return launch_attn_fwd(a, stream);
+}
+
+extern "C" int tri_attn_prefill_heads(const tri_attn_tensors* t, const tri_mask_params* mp,
+                                      const int32_t* d_head_sink, const int32_t* d_head_window,
+                                      const int32_t* d_row_ptr, const int32_t* d_k_tile,
+                                      const uint8_t* d_flags, void* stream) {
+  clear_error();
+  int st = validate_mask(mp);
+  if (st != TRI_OK) return st;
+  if ((st = validate_tensors(t)) != TRI_OK) return st;
+  if (mp->kind != TRI_MASK_TRIANGLE)
+    return fail(TRI_ERR_INVALID, "per-head boundaries apply to the triangle mask");
+  if (mp->block_q != TRI_KERNEL_BLOCK_Q || mp->block_k != TRI_KERNEL_BLOCK_K)
+    return fail(TRI_ERR_UNSUPPORTED, "the kernel walks %dx%d tiles; plan has %dx%d",
+                TRI_KERNEL_BLOCK_Q, TRI_KERNEL_BLOCK_K, mp->block_q, mp->block_k);
+  if (mp->seqlen != t->seqlen)
+    return fail(TRI_ERR_INVALID, "mask seqlen %lld differs from tensor seqlen %lld",
+                static_cast<long long>(mp->seqlen), static_cast<long long>(t->seqlen));
+  if (!d_head_sink || !d_head_window || !d_row_ptr || !d_k_tile || !d_flags)
+    return fail(TRI_ERR_INVALID, "per-head arrays and plan arrays must be non-NULL");
+  if (!aligned(d_head_sink, 4) || !aligned(d_head_window, 4) || !aligned(d_row_ptr, 4) ||
+      !aligned(d_k_tile, 4))
+    return fail(TRI_ERR_INVALID, "int32 arrays must be 4-byte aligned");
+  if (t->seqlen == 0) return TRI_OK;
+  const int64_t nq = (t->seqlen + TRI_KERNEL_BLOCK_Q - 1) / TRI_KERNEL_BLOCK_Q;
+  AttnLaunch a = make_launch(t, false, mp->sink, mp->window, mp->last_q);
+  a.row_ptr = d_row_ptr;
+  a.k_tile = d_k_tile;
+  a.flags = d_flags;
+  a.list_batch_rows = 0;
+  a.list_head_rows = static_cast<int32_t>(nq);
+  a.head_sink = d_head_sink;
+  a.head_window = d_head_window;
   return launch_attn_fwd(a, stream);
 }

@@ -402,15 +402,22 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
     ln.v_dma[i] = static_cast<uint32_t>(min(row, kHalf - 1) * vs_b) + chunk * 16;
   }
 
-  // mask bounds of this lane's row: j <= hi_lim and (j < sink_lim or j >= win_lo)
+  // mask bounds of this lane's row: j <= hi_lim and (j < sink_lim or j >= win_lo);
+  // per-head boundaries, when given, replace the layer's sink and window
+  int head_sink = a.sink, head_window = a.window;
+  if (a.head_sink) {
+    head_sink = min(max(a.head_sink[w.h], 0), N);
+    head_window = max(1, min(a.head_window[w.h], N));
+  }
   ln.hi_lim = min(ln.qrow, N - 1);
   if (kCausal || ln.qrow >= N - a.last_q) {
     ln.sink_lim = 0;
     ln.win_lo = 0;
   } else {
-    ln.sink_lim = a.sink;
-    ln.win_lo = ln.qrow - a.window + 1;
+    ln.sink_lim = head_sink;
+    ln.win_lo = ln.qrow - head_window + 1;
   }
+
 
   // kept tiles of this query tile
   int e_begin, e_end;
@@ -418,9 +425,7 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
     e_begin = 0;
     e_end = (min(N, q0 + kBlockQ) - 1) / kBlockK + 1;
   } else {
-    const int64_t r = a.list_rows_per_head == 0
-                          ? w.t
-                          : (static_cast<int64_t>(w.b) * a.sched.heads_q + w.h) * a.list_rows_per_head + w.t;
+    const int64_t r = w.b * a.list_batch_rows + static_cast<int64_t>(w.h) * a.list_head_rows + w.t;
     e_begin = a.row_ptr[r];
     e_end = a.row_ptr[r + 1];
   }

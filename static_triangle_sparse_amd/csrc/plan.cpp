@@ -149,3 +149,67 @@ extern "C" int tri_attn_plan(const tri_mask_params* mp, int32_t* row_ptr, int32_
   }
   return TRI_OK;
 }
+
+extern "C" int tri_attn_plan_heads(const tri_mask_params* mp, int32_t heads, const int64_t* sink,
+                                   const int64_t* window, int32_t* row_ptr, int32_t* k_tile,
+                                   uint8_t* flags, int64_t capacity, int32_t* n_qtiles_out,
+                                   int64_t* nnz_out) {
+  clear_error();
+  int st = validate_mask(mp);
+  if (st != TRI_OK) return st;
+  if (mp->kind != TRI_MASK_TRIANGLE)
+    return fail(TRI_ERR_INVALID, "per-head boundaries apply to the triangle mask");
+  if (heads < 1) return fail(TRI_ERR_INVALID, "heads must be >= 1");
+  if (!sink || !window) return fail(TRI_ERR_INVALID, "sink and window arrays must be non-NULL");
+  if (!n_qtiles_out || !nnz_out)
+    return fail(TRI_ERR_INVALID, "n_qtiles_out and nnz_out must be non-NULL");
+  const bool sizing = !row_ptr && !k_tile && !flags;
+  if (!sizing && (!row_ptr || !k_tile || !flags))
+    return fail(TRI_ERR_INVALID, "row_ptr, k_tile and flags must be all NULL (sizing) or all non-NULL");
+  if (!sizing && capacity < 0) return fail(TRI_ERR_INVALID, "capacity must be >= 0");
+  for (int32_t h = 0; h < heads; ++h) {
+    if (sink[h] < 0) return fail(TRI_ERR_INVALID, "sink[%d] must be >= 0", h);
+    if (window[h] < 1) return fail(TRI_ERR_INVALID, "window[%d] must be >= 1", h);
+    if (sink[h] > INT32_MAX || window[h] > INT32_MAX)
+      return fail(TRI_ERR_UNSUPPORTED, "sink[%d] and window[%d] must fit in int32", h, h);
+  }
+  const int64_t nq = (mp->seqlen + mp->block_q - 1) / mp->block_q;
+  if (nq * heads >= INT32_MAX) return fail(TRI_ERR_UNSUPPORTED, "too many list rows for int32");
+  int64_t nnz = 0;
+  for (int32_t h = 0; h < heads; ++h) {
+    tri_mask_params m = *mp;
+    m.sink = sink[h];
+    m.window = window[h];
+    for (int64_t t = 0; t < nq; ++t) {
+      TileRange r[2];
+      const int n = kept_ranges(m, t, r);
+      for (int e = 0; e < n; ++e) nnz += r[e].hi - r[e].lo + 1;
+    }
+  }
+  *n_qtiles_out = static_cast<int32_t>(nq);
+  *nnz_out = nnz;
+  if (nnz >= INT32_MAX) return fail(TRI_ERR_UNSUPPORTED, "plan has more than 2^31-1 entries");
+  if (sizing) return TRI_OK;
+  if (capacity < nnz)
+    return fail(TRI_ERR_CAPACITY, "capacity %lld is smaller than the plan's %lld entries",
+                static_cast<long long>(capacity), static_cast<long long>(nnz));
+  int64_t e = 0;
+  row_ptr[0] = 0;
+  for (int32_t h = 0; h < heads; ++h) {
+    tri_mask_params m = *mp;
+    m.sink = sink[h];
+    m.window = window[h];
+    for (int64_t t = 0; t < nq; ++t) {
+      TileRange r[2];
+      const int n = kept_ranges(m, t, r);
+      for (int x = 0; x < n; ++x) {
+        for (int64_t kt = r[x].lo; kt <= r[x].hi; ++kt, ++e) {
+          k_tile[e] = static_cast<int32_t>(kt);
+          flags[e] = tile_flag(m, t, kt);
+        }
+      }
+      row_ptr[h * nq + t + 1] = static_cast<int32_t>(e);
+    }
+  }
+  return TRI_OK;
+}

@@ -131,9 +131,15 @@ struct AttnLaunch {
   const int32_t* row_ptr;
   const int32_t* k_tile;
   const uint8_t* flags;
-  // 0: one list shared by every (batch, head), row t; n > 0: per-head lists,
-  // row (b * heads_q + h) * n + t (n = query tiles)
-  int32_t list_rows_per_head;
+  // list row of (batch b, head h, query tile t):
+  //   b * list_batch_rows + h * list_head_rows + t
+  // (0, 0): one list for every (batch, head); (0, nq): per-head lists shared
+  // by the batch; (heads_q * nq, nq): per-(batch, head) lists
+  int64_t list_batch_rows;
+  int32_t list_head_rows;
+  // per-head sink and window (device, [heads_q]), or NULL for the layer's
+  const int32_t* head_sink;
+  const int32_t* head_window;
   Schedule sched;
 };
 

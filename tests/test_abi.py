@@ -24,7 +24,7 @@ def test_header_symbols_are_exported():
     names = _declared_functions()
     assert {"tri_attn_plan", "tri_attn_prefill", "dense_causal_prefill",
             "tri_attn_last_error", "tri_dyn_plan_sizes", "tri_dyn_plan",
-            "tri_attn_prefill_lists"} <= set(names)
+            "tri_attn_prefill_lists", "tri_attn_plan_heads", "tri_attn_prefill_heads"} <= set(names)
     lib = ctypes.CDLL(_abi.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -223,6 +223,28 @@ def test_prefill_lists_rejects_bad_arguments():
     assert lib.tri_attn_prefill_lists(ctypes.byref(t), P, P, None, None) == tsa.TRI_ERR_INVALID
     assert lib.tri_attn_prefill_lists(ctypes.byref(t), P + 1, P, P, None) == tsa.TRI_ERR_INVALID
     assert lib.tri_attn_prefill_lists(ctypes.byref(_good_tensors(N=0)), P, P, P, None) == tsa.TRI_OK
+
+
+def test_prefill_heads_rejects_bad_arguments():
+    lib = _abi.load()
+    t = _good_tensors()
+    mp = tsa.mask_params(256, "triangle", 4, 64, 16)
+    P = 1 << 24
+    args = [P, P, P, P, P]  # a valid call would launch: only the error paths run here
+    for i in range(5):
+        bad = list(args)
+        bad[i] = None
+        assert lib.tri_attn_prefill_heads(ctypes.byref(t), ctypes.byref(mp), *bad, None) == tsa.TRI_ERR_INVALID
+    bad = list(args)
+    bad[0] = P + 2
+    assert lib.tri_attn_prefill_heads(ctypes.byref(t), ctypes.byref(mp), *bad, None) == tsa.TRI_ERR_INVALID
+    causal = tsa.mask_params(256, "causal")
+    assert lib.tri_attn_prefill_heads(ctypes.byref(t), ctypes.byref(causal), *args, None) == tsa.TRI_ERR_INVALID
+    other = tsa.mask_params(255, "triangle", 4, 64, 16)
+    assert lib.tri_attn_prefill_heads(ctypes.byref(t), ctypes.byref(other), *args, None) == tsa.TRI_ERR_INVALID
+    z = _good_tensors(N=0)
+    mz = tsa.mask_params(0, "triangle", 4, 64, 16)
+    assert lib.tri_attn_prefill_heads(ctypes.byref(z), ctypes.byref(mz), *args, None) == tsa.TRI_OK
 
 
 # ----------------------------------------------------------------- schedule

@@ -84,3 +84,42 @@ def test_kernel_causal_range_rule():
 def test_empty_sequence():
     row_ptr, k_tile, flags = _plan(0, 128, 64, "triangle", 1, 1, 1)
     assert row_ptr.tolist() == [0] and k_tile.size == 0 and flags.size == 0
+
+
+# ------------------------------------------------------ per-head boundaries
+
+@pytest.mark.parametrize("N,bq,bk,last_q", [(300, 32, 16, 20), (1000, 128, 64, 64), (129, 128, 64, 0),
+                                            (5000, 128, 64, 128)])
+def test_per_head_plan_is_the_brute_force_plan_of_each_head(N, bq, bk, last_q):
+    # head h's rows of the per-head CSR are the oracle's tile list for that
+    # head's (sink, window) -- TriAttention page: per-head boundaries
+    heads = [(0, 1), (4, 100), (200, N + 5), (N + 1, 3), (17, 33), (64, 2048)]
+    sink = [s for s, _ in heads]
+    window = [w for _, w in heads]
+    rp, kt, fl = tsa.tri_attn_plan_heads(tsa.mask_params(N, "triangle", 0, 1, last_q, bq, bk),
+                                         sink, window)
+    nq = -(-N // bq)
+    assert rp.size == len(heads) * nq + 1
+    for h, (s, w) in enumerate(heads):
+        ref = (omask.brute_tiles(N, bq, bk, "triangle", s, w, last_q) if N <= 1000 else
+               omask.interval_tiles(N, bq, bk, "triangle", s, w, last_q))
+        seg = slice(rp[h * nq], rp[(h + 1) * nq])
+        assert np.array_equal(kt[seg], ref[1]) and np.array_equal(fl[seg], ref[2]), (h, s, w)
+        assert np.array_equal(rp[h * nq:(h + 1) * nq + 1] - rp[h * nq], ref[0])
+
+
+def test_per_head_plan_rejects_bad_arguments():
+    import ctypes
+    lib = tsa.load()
+    mp = tsa.mask_params(500, "triangle", 0, 1, 0)
+    A = lambda x: (ctypes.c_int64 * len(x))(*x)
+    nq, nnz = ctypes.c_int32(), ctypes.c_int64()
+    call = lambda m, H, s, w: lib.tri_attn_plan_heads(ctypes.byref(m), H, s, w, None, None, None, 0,
+                                                      ctypes.byref(nq), ctypes.byref(nnz))
+    assert call(mp, 2, A([1, 2]), A([3, 4])) == tsa.TRI_OK
+    assert call(mp, 0, A([1]), A([3])) == tsa.TRI_ERR_INVALID
+    assert call(mp, 2, A([1, -1]), A([3, 4])) == tsa.TRI_ERR_INVALID
+    assert call(mp, 2, A([1, 2]), A([3, 0])) == tsa.TRI_ERR_INVALID
+    assert call(mp, 1, None, A([3])) == tsa.TRI_ERR_INVALID
+    assert call(tsa.mask_params(500, "causal"), 1, A([1]), A([3])) == tsa.TRI_ERR_INVALID
+    assert call(mp, 1, A([1 << 40]), A([3])) == tsa.TRI_ERR_UNSUPPORTED
