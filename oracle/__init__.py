@@ -22,6 +22,9 @@ What it computes (all in float64, from the exact bf16 input values):
                    (probe queries against pooled keys, max-based threshold;
                    FlashPrefill page, sections 2.1-2.3) and attention over an
                    explicit per-head tile list.
+* ``tiers``     -- triangle attention with fp8 (e4m3) scores on tiles past a
+                   per-head diagonal-distance boundary (TriAttention page),
+                   with its e4m3 rounding and block scales.
 
 Sources (the pages this method is described on):
   * "TriangleMix" blog post (PaperWeekly / news.fishai.com.cn), sections
@@ -32,8 +35,8 @@ Sources (the pages this method is described on):
     "Last Q-K" aggregation region are kept; complexity falls to O(N).
 
 Every function here is pinned by tests in ``tests/test_oracle_pins.py`` and
-``tests/test_oracle_dynamic.py``
+``tests/test_oracle_dynamic.py`` and ``tests/test_oracle_tiers.py``
 (brute force, closed forms, library attention on the special cases that
 reduce to it, and hand-derived tile grids); none is "parity unpinned".
 """
-from . import mask, attention, brute, dynamic  # noqa: F401
+from . import mask, attention, brute, dynamic, tiers  # noqa: F401

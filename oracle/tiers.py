@@ -1,0 +1,132 @@
+"""Precision tiers for the triangle layer: far tiles scored with fp8 Q and K.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Source: the TriAttention page.  It assigns each query-key tile to skipping,
+a lower-precision or a higher-precision score computation, chooses the
+regions per head with two diagonal-distance boundaries, and combines the
+contributions of both precisions into one normalised attention output.  On
+MI355X the native lower-precision matrix format is fp8 (e4m3); the layer's
+skipping is the triangle plan itself, so one per-head boundary remains:
+
+* a kept key tile kt of query tile t is LOW precision when its smallest
+  query-key distance, t*Bq - (kt*Bk + Bk - 1), is >= dist[h]; otherwise it
+  is computed in bf16 as in the plain triangle layer;
+* on LOW tiles the score is scale * s_q * s_k * <q8, k8>, with
+    - s_q = amax(|q row|) / 448 and q8 = e4m3(q * (448 / amax)),
+    - s_k = amax(|K of the 32-key half-tile|) / 448 and
+      k8 = e4m3(k * (448 / amax)),
+  every scale and product formed in float32 as the GPU forms them (the
+  rounding of a value to a code is an integer decision: both sides take it
+  in the same precision); an all-zero row or half-tile has scale 0;
+* values are then combined in one softmax over the row's kept keys.
+
+P and V stay bf16 (only the scores change precision); the oracle's softmax
+and PV are float64.  Pins: tests/test_oracle_tiers.py.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from . import mask as _mask
+
+E4M3_MAX = 448.0
+
+
+def e4m3_values():
+    """All 256 e4m3 codes decoded (NaN for the two NaN codes 0x7F, 0xFF)."""
+    out = np.empty(256)
+    for c in range(256):
+        s = -1.0 if c & 0x80 else 1.0
+        e = (c >> 3) & 0xF
+        m = c & 0x7
+        if e == 0xF and m == 0x7:
+            out[c] = np.nan
+        elif e == 0:
+            out[c] = s * m / 8.0 * 2.0 ** -6
+        else:
+            out[c] = s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return out
+
+
+def round_e4m3(x):
+    """Round float32 values to e4m3 (nearest, ties to even), saturating at
+    +-448.  Returns float64 values of the chosen codes."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    # exponent of the binade (normal: 2^-6 .. 2^8); below 2^-6 the subnormal
+    # step 2^-9 applies
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)
+    step = 2.0 ** (e - 3)
+    q = a / step
+    r = np.floor(q)
+    frac = q - r
+    up = (frac > 0.5) | ((frac == 0.5) & (np.mod(r, 2) == 1))
+    v = (r + up) * step
+    return np.copysign(np.minimum(v, E4M3_MAX), x)
+
+
+def quantize(x, axis=None):
+    """(codes as float64 values, scale) of a block: float32 arithmetic as on
+    the GPU.  ``axis``: reduce amax over this axis (keepdims)."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x32), axis=axis, keepdims=axis is not None).astype(np.float32)
+    with np.errstate(divide="ignore"):
+        inv = np.where(amax > 0, np.float32(E4M3_MAX) / amax, np.float32(0)).astype(np.float32)
+    y = (x32 * inv).astype(np.float32)
+    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    return round_e4m3(y), scale
+
+
+def low_tile(t, kt, dist, block_q=128, block_k=64):
+    """True when key tile kt of query tile t is computed in fp8."""
+    return t * block_q - (kt * block_k + block_k - 1) >= dist
+
+
+def attention(q, k, v, sink, window, last_q, dist, scale=None, rows=None, block_q=128, block_k=64):
+    """Triangle attention with fp8 scores on far tiles.
+
+    q [B, Hq, N, d], k/v [B, Hkv, N, d] (exact bf16 values); dist: per query
+    head boundary (list of Hq ints).  Returns (o [B, Hq, R, d], lse [B, Hq, R])
+    for the requested rows (default all), float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rows = np.arange(N) if rows is None else np.asarray(rows, np.int64)
+    half = block_k // 2
+    nh = -(-N // half)
+    # fp8 keys per 32-key half-tile (keys >= N are zero, as the GPU loads them)
+    kp = np.zeros((B, Hkv, nh * half, d))
+    kp[:, :, :N] = k
+    kq, ks = quantize(kp.reshape(B, Hkv, nh, half * d), axis=3)
+    k8 = kq.reshape(B, Hkv, nh * half, d)[:, :, :N]
+    s_k = np.repeat(ks[..., 0], half, axis=2)[:, :, :N]               # [B, Hkv, N]
+    o = np.zeros((B, Hq, rows.size, d))
+    lse = np.zeros((B, Hq, rows.size))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            for n, i in enumerate(rows):
+                keys = _mask.kept_keys(i, N, "triangle", sink, window, last_q)
+                q8, s_q = quantize(q[b, h, i])
+                t = i // block_q
+                low = low_tile(t, keys // block_k, dist[h], block_q, block_k)
+                z_hi = scale * (k[b, g, keys] @ q[b, h, i])
+                acc = k8[b, g, keys] @ q8
+                z_lo = scale * (np.float64(s_q) * s_k[b, g, keys]) * acc
+                z = np.where(low, z_lo, z_hi)
+                m = z.max()
+                p = np.exp(z - m)
+                l = p.sum()
+                o[b, h, n] = p @ v[b, g, keys] / l
+                lse[b, h, n] = m + math.log(l)
+    return o, lse
