@@ -211,6 +211,36 @@ def bench_per_head(t, args, cfg, d, Hq, B, dev, stream):
             "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
 
 
+def bench_tiered(t, args, cfg, plan, tri_ms, d, Hq, B, dev, stream):
+    """The triangle layer with precision tiers (TriAttention page: per-head
+    diagonal-distance boundaries choose each tile's precision): key tiles at
+    least --low-dist keys behind the query tile scored in fp8 (e4m3), the
+    rest in bf16.  K's fp8 copy and the layer are timed separately."""
+    import numpy as np
+    import torch
+    import static_triangle_sparse_amd as tsa
+    qk = tsa.QuantizedK(t, dev)
+    quant_ms, _ = time_launches(lambda: qk.run(t, stream), args.dense_steps, 1)
+    dist = np.full(Hq, args.low_dist, np.int32)
+    d_dist = torch.from_numpy(dist).to(dev)
+    run = lambda: tsa.tri_attn_prefill_tiered(t, plan.mp, d_dist.data_ptr(), qk.k8.data_ptr(),
+                                              qk.scale.data_ptr(), plan.d_row_ptr.data_ptr(),
+                                              plan.d_k_tile.data_ptr(), plan.d_flags.data_ptr(), stream)
+    ms, _ = time_launches(run, args.steps, args.warmup)
+    rows = np.repeat(np.arange(plan.row_ptr.size - 1), np.diff(plan.row_ptr))
+    n_low = int(np.sum(rows * 128 - (plan.k_tile.astype(np.int64) * 64 + 63) >= args.low_dist))
+    frac = n_low / max(1, plan.k_tile.size)
+    flops = 4.0 * 128 * 64 * d * plan.k_tile.size * Hq * B
+    tf = flops / (ms * 1e-3) / 1e12
+    print(f"[bench] tiered triangle (fp8 scores from distance {args.low_dist}): K to fp8 "
+          f"{quant_ms:.3f} ms + layer {ms:.3f} ms, {100 * frac:.1f}% of tiles fp8",
+          file=sys.stderr, flush=True)
+    return {"low_dist": args.low_dist, "low_tile_fraction": round(frac, 4),
+            "quantize_ms": round(quant_ms, 4), "attention_ms": round(ms, 4),
+            "kept_tflops": round(tf, 2), "speedup_vs_bf16_triangle": round(tri_ms / ms, 3),
+            "speedup_incl_quantize": round(tri_ms / (ms + quant_ms), 3)}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +253,9 @@ def main(argv=None):
                     help="also time the triangle layer with per-head windows (0: skip)")
     ap.add_argument("--dyn-alpha", type=float, default=0.9,
                     help="keep threshold of the dynamic block-sparse dense layer (0 disables it)")
+    ap.add_argument("--low-dist", type=int, default=1024,
+                    help="precision tiers: fp8 scores on key tiles at least this many keys behind "
+                         "the query tile (negative: disable the tiered layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
@@ -277,6 +310,8 @@ def main(argv=None):
             extra["dynamic_dense"] = bench_dynamic(t, args, dense_ms, d, Hq, B, dev, stream)
         if args.per_head:
             extra["per_head_triangle"] = bench_per_head(t, args, cfg, d, Hq, B, dev, stream)
+        if args.low_dist >= 0:
+            extra["tiered_triangle"] = bench_tiered(t, args, cfg, plan, tri_ms, d, Hq, B, dev, stream)
 
     if args.calib_copy_mib:
         nbytes = args.calib_copy_mib << 20

@@ -233,6 +233,36 @@ int tri_attn_prefill_heads(const tri_attn_tensors* t, const tri_mask_params* mp,
                            const int32_t* d_row_ptr, const int32_t* d_k_tile,
                            const uint8_t* d_flags, void* stream);
 
+/*
+ * Precision tiers.  The TriAttention page scores query-key tiles at two
+ * precisions, chosen per head by diagonal-distance boundaries, and combines
+ * both groups in one normalised output.  Here the lower tier is fp8 (e4m3)
+ * on MI355X's fp8 matrix cores, for the scores only (P and V stay bf16): a
+ * kept key tile kt of query tile t is LOW when 128*t - (64*kt + 63) >=
+ * low_dist[h] (every query-key distance in the tile reaches the boundary).
+ * A LOW tile's score is softmax_scale * s_q * s_k * <q8, k8>, with
+ *   s_q = amax |q row| / 448,           q8 = e4m3(q * (448 / amax_q)),
+ *   s_k = amax |K of the 32-key half| / 448, k8 = e4m3(k * (448 / amax_k)),
+ * rounded to nearest even after clamping to +-448 (all-zero blocks: scale 0).
+ *
+ * tri_attn_quantize_k_sizes -- bytes of the fp8 K (batch*heads_kv*N*head_dim)
+ * and number of scales (batch*heads_kv*ceil(N/32)).
+ * tri_attn_quantize_k -- enqueue the fp8 copy of t->k: d_k8 (16-byte
+ * aligned) holds, for each (batch, KV head), N rows of head_dim bytes in the
+ * kernel's operand order (byte 64s + 32h + j of a row is channel
+ * 64s + 16(j/8) + 8h + j%8); d_scale [batch, heads_kv, ceil(N/32)] f32.
+ * tri_attn_prefill_tiered -- tri_attn_prefill with the LOW tiles scored from
+ * d_k8 / d_scale (the output of tri_attn_quantize_k for the same K) and the
+ * device int32 boundaries d_head_low_dist [heads_q]; Q is quantized in the
+ * kernel.  A boundary larger than N gives the plain triangle layer.
+ */
+int tri_attn_quantize_k_sizes(const tri_attn_tensors* t, int64_t* k8_bytes, int64_t* n_scales);
+int tri_attn_quantize_k(const tri_attn_tensors* t, void* d_k8, float* d_scale, void* stream);
+int tri_attn_prefill_tiered(const tri_attn_tensors* t, const tri_mask_params* mp,
+                            const int32_t* d_head_low_dist, const void* d_k8, const float* d_scale,
+                            const int32_t* d_row_ptr, const int32_t* d_k_tile,
+                            const uint8_t* d_flags, void* stream);
+
 /* Message for the last non-OK return on this thread ("" if none). */
 const char* tri_attn_last_error(void);
 

@@ -24,7 +24,8 @@ from ._abi import (  # noqa: F401
     TRI_MASK_TRIANGLE, TRI_OK, TRI_TILE_FULL, TRI_TILE_PARTIAL, TRI_DYN_PROBES, AttnTensors,
     DynParams, MaskParams, TriAttnError, dense_causal_prefill, last_error, load, mask_params,
     tri_attn_abi_version, tri_attn_plan, tri_attn_plan_heads, tri_attn_prefill,
-    tri_attn_prefill_heads, tri_attn_prefill_lists, tri_attn_work_item, tri_dyn_plan,
+    tri_attn_prefill_heads, tri_attn_prefill_lists, tri_attn_prefill_tiered,
+    tri_attn_quantize_k, tri_attn_quantize_k_sizes, tri_attn_work_item, tri_dyn_plan,
     tri_dyn_plan_sizes,
 )
 
@@ -33,6 +34,7 @@ __all__ = [
     "dense_causal_prefill", "mask_params", "TriAttnError", "last_error", "layer_mode",
     "DynPlan", "dyn_plan", "tri_dyn_plan", "tri_dyn_plan_sizes", "tri_attn_prefill_lists",
     "HeadPlan", "head_plan", "tri_attn_plan_heads", "tri_attn_prefill_heads",
+    "QuantizedK", "quantize_k", "tri_attn_quantize_k", "tri_attn_prefill_tiered",
 ]
 
 
@@ -131,6 +133,30 @@ def head_plan(seqlen, sink, window, last_q=0, device="cuda") -> HeadPlan:
     return HeadPlan(seqlen, sink, window, last_q, device)
 
 
+class QuantizedK:
+    """fp8 copy of K for the precision tiers (device uint8 k8, f32 scales)."""
+
+    def __init__(self, t: AttnTensors, device):
+        import torch
+        nbytes, nscales = tri_attn_quantize_k_sizes(t)
+        self.k8 = torch.empty(max(16, nbytes), dtype=torch.uint8, device=device)
+        self.scale = torch.empty(max(1, nscales), dtype=torch.float32, device=device)
+
+    def run(self, t: AttnTensors, stream: int) -> None:
+        tri_attn_quantize_k(t, self.k8.data_ptr(), self.scale.data_ptr(), stream)
+
+
+def quantize_k(q, k, stream=None) -> QuantizedK:
+    """fp8 (e4m3) copy of k in the tiered kernel's layout, with its scales."""
+    import torch
+    o = torch.empty((1, 1, 1, 8), dtype=torch.bfloat16, device=k.device)  # not written
+    t = make_tensors(q, k, k, o, None)
+    qk = QuantizedK(t, k.device)
+    s = (stream if stream is not None else torch.cuda.current_stream(k.device)).cuda_stream
+    qk.run(t, s)
+    return qk
+
+
 class DynPlan:
     """Device buffers of a dynamic block-sparse plan (tri_dyn_plan): workspace,
     row_ptr [n_rows + 1], k_tile and flags [max_nnz], all torch tensors."""
@@ -163,7 +189,7 @@ def dyn_plan(q, k, alpha, scale=None, stream=None) -> DynPlan:
 
 
 def prefill(q, k, v, mode="triangle", sink=0, window=1, last_q=0, o_dtype=None, scale=None,
-            out=None, lse=None, stream=None, plan=None):
+            out=None, lse=None, stream=None, plan=None, low_dist=None):
     """One attention layer on the GPU; returns (o, lse).  ``mode`` is
     "triangle" (planned tile list), "causal" (dense layer) or "lists"
     (per-head tile lists of a DynPlan, causal mask inside the tiles)."""
@@ -189,6 +215,19 @@ def prefill(q, k, v, mode="triangle", sink=0, window=1, last_q=0, o_dtype=None, 
         tri_attn_prefill_heads(t, plan.mp, plan.d_sink.data_ptr(), plan.d_window.data_ptr(),
                                plan.d_row_ptr.data_ptr(), plan.d_k_tile.data_ptr(),
                                plan.d_flags.data_ptr(), s)
+    elif mode == "tiered":
+        if plan is None or low_dist is None:
+            raise ValueError("mode 'tiered' needs plan= (a QuantizedK of k) and low_dist=")
+        import torch
+        p = device_plan(N, "triangle", sink, window, last_q, q.device)
+        # the device copy of the boundaries lives on the QuantizedK object, so it
+        # outlives the enqueued kernel
+        plan.low_dist = torch.as_tensor(
+            np.minimum(np.asarray(low_dist, np.int64), np.iinfo(np.int32).max),
+            dtype=torch.int32).to(q.device)
+        tri_attn_prefill_tiered(t, p.mp, plan.low_dist.data_ptr(), plan.k8.data_ptr(),
+                                plan.scale.data_ptr(), p.d_row_ptr.data_ptr(), p.d_k_tile.data_ptr(),
+                                p.d_flags.data_ptr(), s)
     elif mode == "lists":
         if plan is None:
             raise ValueError("mode 'lists' needs plan= (a DynPlan)")

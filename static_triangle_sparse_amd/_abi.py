@@ -135,6 +135,15 @@ def load() -> ctypes.CDLL:
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_void_p]
     lib.tri_attn_prefill_heads.restype = ctypes.c_int
+    lib.tri_attn_quantize_k_sizes.argtypes = [P(AttnTensors), P(ctypes.c_int64), P(ctypes.c_int64)]
+    lib.tri_attn_quantize_k_sizes.restype = ctypes.c_int
+    lib.tri_attn_quantize_k.argtypes = [P(AttnTensors), ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    lib.tri_attn_quantize_k.restype = ctypes.c_int
+    lib.tri_attn_prefill_tiered.argtypes = [P(AttnTensors), P(MaskParams), ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.tri_attn_prefill_tiered.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -260,3 +269,24 @@ def tri_attn_prefill_heads(t: AttnTensors, mp: MaskParams, d_head_sink: int, d_h
     """Enqueue a triangle layer with per-head boundaries (device pointers)."""
     _check(load().tri_attn_prefill_heads(ctypes.byref(t), ctypes.byref(mp), d_head_sink,
                                          d_head_window, d_row_ptr, d_k_tile, d_flags, stream))
+
+
+def tri_attn_quantize_k_sizes(t: AttnTensors):
+    """(bytes of the fp8 K, number of f32 scales) for layer ``t``."""
+    nb = ctypes.c_int64()
+    ns = ctypes.c_int64()
+    _check(load().tri_attn_quantize_k_sizes(ctypes.byref(t), ctypes.byref(nb), ctypes.byref(ns)))
+    return nb.value, ns.value
+
+
+def tri_attn_quantize_k(t: AttnTensors, d_k8: int, d_scale: int, stream: int) -> None:
+    """Enqueue the fp8 copy of t.k (device pointers)."""
+    _check(load().tri_attn_quantize_k(ctypes.byref(t), d_k8, d_scale, stream))
+
+
+def tri_attn_prefill_tiered(t: AttnTensors, mp: MaskParams, d_low_dist: int, d_k8: int,
+                            d_scale: int, d_row_ptr: int, d_k_tile: int, d_flags: int,
+                            stream: int) -> None:
+    """Enqueue a triangle layer with fp8 scores on far tiles (device pointers)."""
+    _check(load().tri_attn_prefill_tiered(ctypes.byref(t), ctypes.byref(mp), d_low_dist, d_k8,
+                                          d_scale, d_row_ptr, d_k_tile, d_flags, stream))

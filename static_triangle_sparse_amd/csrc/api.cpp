@@ -341,3 +341,70 @@ extern "C" int tri_attn_prefill_heads(const tri_attn_tensors* t, const tri_mask_
   a.head_window = d_head_window;
   return launch_attn_fwd(a, stream);
 }
+
+extern "C" int tri_attn_quantize_k_sizes(const tri_attn_tensors* t, int64_t* k8_bytes,
+                                         int64_t* n_scales) {
+  clear_error();
+  int st = validate_tensors(t);
+  if (st != TRI_OK) return st;
+  if (!k8_bytes || !n_scales) return fail(TRI_ERR_INVALID, "output pointers must be non-NULL");
+  *k8_bytes = static_cast<int64_t>(t->batch) * t->heads_kv * t->seqlen * t->head_dim;
+  *n_scales = static_cast<int64_t>(t->batch) * t->heads_kv * ((t->seqlen + 31) / 32);
+  return TRI_OK;
+}
+
+extern "C" int tri_attn_quantize_k(const tri_attn_tensors* t, void* d_k8, float* d_scale,
+                                   void* stream) {
+  clear_error();
+  int st = validate_tensors(t);
+  if (st != TRI_OK) return st;
+  if (!d_k8 || !d_scale) return fail(TRI_ERR_INVALID, "d_k8 and d_scale must be non-NULL");
+  if (!aligned(d_k8, 16) || !aligned(d_scale, 4))
+    return fail(TRI_ERR_INVALID, "d_k8 must be 16-byte and d_scale 4-byte aligned");
+  if (t->seqlen == 0) return TRI_OK;
+  QuantLaunch a{};
+  a.k = t->k;
+  memcpy(a.k_stride, t->k_stride, sizeof(a.k_stride));
+  a.heads_kv = t->heads_kv;
+  a.head_dim = t->head_dim;
+  a.seqlen = static_cast<int32_t>(t->seqlen);
+  a.n_blocks = static_cast<int64_t>(t->batch) * t->heads_kv * ((t->seqlen + 31) / 32);
+  a.k8 = d_k8;
+  a.scale = d_scale;
+  return launch_quantize_k(a, stream);
+}
+
+extern "C" int tri_attn_prefill_tiered(const tri_attn_tensors* t, const tri_mask_params* mp,
+                                       const int32_t* d_head_low_dist, const void* d_k8,
+                                       const float* d_scale, const int32_t* d_row_ptr,
+                                       const int32_t* d_k_tile, const uint8_t* d_flags,
+                                       void* stream) {
+  clear_error();
+  int st = validate_mask(mp);
+  if (st != TRI_OK) return st;
+  if ((st = validate_tensors(t)) != TRI_OK) return st;
+  if (mp->kind != TRI_MASK_TRIANGLE)
+    return fail(TRI_ERR_INVALID, "precision tiers apply to the triangle mask");
+  if (mp->block_q != TRI_KERNEL_BLOCK_Q || mp->block_k != TRI_KERNEL_BLOCK_K)
+    return fail(TRI_ERR_UNSUPPORTED, "the kernel walks %dx%d tiles; plan has %dx%d",
+                TRI_KERNEL_BLOCK_Q, TRI_KERNEL_BLOCK_K, mp->block_q, mp->block_k);
+  if (mp->seqlen != t->seqlen)
+    return fail(TRI_ERR_INVALID, "mask seqlen %lld differs from tensor seqlen %lld",
+                static_cast<long long>(mp->seqlen), static_cast<long long>(t->seqlen));
+  if (!d_head_low_dist || !d_k8 || !d_scale || !d_row_ptr || !d_k_tile || !d_flags)
+    return fail(TRI_ERR_INVALID, "boundary, fp8 K, scale and plan arrays must be non-NULL");
+  if (!aligned(d_head_low_dist, 4) || !aligned(d_k8, 16) || !aligned(d_scale, 4) ||
+      !aligned(d_row_ptr, 4) || !aligned(d_k_tile, 4))
+    return fail(TRI_ERR_INVALID, "misaligned array (fp8 K: 16 bytes, int32/float: 4 bytes)");
+  if (t->seqlen * t->head_dim >= (int64_t(1) << 31))
+    return fail(TRI_ERR_UNSUPPORTED, "seqlen x head_dim must be < 2^31 bytes of fp8 K per head");
+  if (t->seqlen == 0) return TRI_OK;
+  AttnLaunch a = make_launch(t, false, mp->sink, mp->window, mp->last_q);
+  a.row_ptr = d_row_ptr;
+  a.k_tile = d_k_tile;
+  a.flags = d_flags;
+  a.k8 = d_k8;
+  a.k8_scale = d_scale;
+  a.head_low_dist = d_head_low_dist;
+  return launch_attn_fwd(a, stream);
+}

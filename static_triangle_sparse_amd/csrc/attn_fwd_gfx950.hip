@@ -48,6 +48,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 #define LDS_AS __attribute__((address_space(3)))
 #define GLOBAL_AS __attribute__((address_space(1)))
@@ -80,6 +81,12 @@ struct Cfg {
   static constexpr int kKBlocksPerWave = (kKBlocks + kWaves - 1) / kWaves;
   static constexpr int kVBlocksPerWave = (kVBlocks + kWaves - 1) / kWaves;
   static constexpr int kStageBytes = kKBytes + kVBytes;
+  // fp8 K of a far (LOW tier) half: 32 rows of D bytes, padded by 16 bytes
+  // (one 16-byte bank step per row), in whole 1 KiB copy blocks
+  static constexpr int kK8Stride = D + 16;
+  static constexpr int kK8Blocks = (kHalf * kK8Stride + 1023) / 1024;
+  static constexpr int kK8BlocksPerWave = (kK8Blocks + kWaves - 1) / kWaves;
+  static constexpr int kQ8Steps = D / 64;  // k-steps of the fp8 S^T
   static constexpr int kQSteps = D / 16;   // k-steps of S^T = K Q^T
   static constexpr int kOBlocks = D / 32;  // 32-channel blocks of O^T
   static_assert(kKBytes % 1024 == 0 && kVBytes % 1024 == 0, "tiles fill whole DMA blocks");
@@ -185,11 +192,27 @@ __device__ __forceinline__ void dma_source(int x, int stride, int& row, int& chu
   if (chunk >= D / 8) chunk = 0;
 }
 
-template <int D, bool kOutBf16, bool kCausal>
+// Quantized Q of the tiered kernel (empty otherwise).
+template <int D, bool kTiers>
+struct TierState {};
+template <int D>
+struct TierState<D, true> {
+  i32x8 q8[Cfg<D>::kQ8Steps];  // fp8 e4m3 Q in the fp8 operand order
+  float s_q;                   // its scale: row amax / 448
+};
+template <int D, bool kTiers>
+struct TierLane {};
+template <int D>
+struct TierLane<D, true> {
+  uint32_t k8_dma[Cfg<D>::kK8BlocksPerWave];
+  int k8_rd;
+};
+
+template <int D, bool kOutBf16, bool kCausal, bool kTiers>
 struct Kernel {
   using C = Cfg<D>;
 
-  struct State {
+  struct State : TierState<D, kTiers> {
     bf16x8 q[C::kQSteps];
     f32x16 o[C::kOBlocks];
     float m;       // reference max of raw scores q.k (fixed once set, see compute_half)
@@ -200,7 +223,7 @@ struct Kernel {
   };
 
   // Per-lane constants of one workgroup.
-  struct Lane {
+  struct Lane : TierLane<D, kTiers> {
     int hi;
     int k_rd;  // K operand read offset (stage-relative bytes)
     int v_rd;  // V^T transposing-read offset (relative to the V tile)
@@ -230,19 +253,64 @@ struct Kernel {
     }
   }
 
+  // fp8 K of a LOW half (blocks of the K region) plus V, as issue_dma.
+  static __device__ __forceinline__ void issue_dma_low(char LDS_AS* stage, const Lane& ln, int wave,
+                                                       const u32x4& k8_rsrc, const u32x4& v_rsrc) {
+    if constexpr (kTiers) {
+#pragma unroll
+      for (int i = 0; i < C::kK8BlocksPerWave; ++i) {
+        const int blk = i * kWaves + wave;
+        if (C::kK8Blocks % kWaves == 0 || blk < C::kK8Blocks)
+          lds_dma16(k8_rsrc, ln.k8_dma[i], stage + blk * 1024);
+      }
+#pragma unroll
+      for (int i = 0; i < C::kVBlocksPerWave; ++i) {
+        const int blk = i * kWaves + wave;
+        if (C::kVBlocks % kWaves == 0 || blk < C::kVBlocks)
+          lds_dma16(v_rsrc, ln.v_dma[i], stage + C::kKBytes + blk * 1024);
+      }
+    }
+  }
+
   // S^T block of one 32-key half (kb): lane = query, 16 of the 32 keys per
   // lane; register r holds key key0 + 32 kb + 8 (r >> 2) + 4 hi + (r & 3).
   // Keys a PARTIAL tile drops are set to -inf.
+  // In the tiered kernel a LOW half (low) is scored from fp8 K and Q with
+  // v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) and rescaled by
+  // s_q s_k (sqk) to raw score units.
   static __device__ __forceinline__ f32x16 scores(const char LDS_AS* stage, const Lane& ln, const State& st,
-                                                  int kb, int key0, bool partial) {
-    const char LDS_AS* kp = stage + ln.k_rd;
+                                                  int kb, int key0, bool partial, bool low = false,
+                                                  float s_k = 0.0f) {
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+    bool done = false;
+    if constexpr (kTiers) {
+      if (low) {
+        const char LDS_AS* kp8 = stage + ln.k8_rd;
 #pragma unroll
-    for (int q = 0; q < C::kQSteps; ++q) {
-      const bf16x8 kv = *reinterpret_cast<const LDS_AS bf16x8*>(kp + q * 32);
-      s = mfma32(kv, st.q[q], s);
+        for (int q = 0; q < C::kQ8Steps; ++q) {
+          const u32x4 a0 = *reinterpret_cast<const LDS_AS u32x4*>(kp8 + q * 64);
+          const u32x4 a1 = *reinterpret_cast<const LDS_AS u32x4*>(kp8 + q * 64 + 16);
+          const i32x8 ka = {static_cast<int>(a0[0]), static_cast<int>(a0[1]), static_cast<int>(a0[2]),
+                            static_cast<int>(a0[3]), static_cast<int>(a1[0]), static_cast<int>(a1[1]),
+                            static_cast<int>(a1[2]), static_cast<int>(a1[3])};
+          s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, st.q8[q], s, 0, 0, 0, 0x7F7F7F7F, 0,
+                                                              0x7F7F7F7F);
+        }
+        const float f = st.s_q * s_k;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] *= f;
+        done = true;
+      }
+    }
+    if (!done) {
+      const char LDS_AS* kp = stage + ln.k_rd;
+#pragma unroll
+      for (int q = 0; q < C::kQSteps; ++q) {
+        const bf16x8 kv = *reinterpret_cast<const LDS_AS bf16x8*>(kp + q * 32);
+        s = mfma32(kv, st.q[q], s);
+      }
     }
     if (partial) {
       // bit o of `drop` is set when key base + o is masked for this lane's row
@@ -282,8 +350,9 @@ struct Kernel {
   // range), reruns the list with each row's exact max as the reference.
   static __device__ __forceinline__ void compute_half(const char LDS_AS* stage, const Lane& ln,
                                                       State& st, int kb, int key0, bool partial,
-                                                      float c_log2, bool& need_ref) {
-    const f32x16 s = scores(stage, ln, st, kb, key0, partial);
+                                                      float c_log2, bool& need_ref, bool low = false,
+                                                      float s_k = 0.0f) {
+    const f32x16 s = scores(stage, ln, st, kb, key0, partial, low, s_k);
     if (need_ref) {
       // a row with no kept key so far has O = 0 and l = 0: its reference may still move
       const float mx = row_max(s);
@@ -345,14 +414,14 @@ struct Kernel {
 
   // Exact-max pass over one 32-key half: scores and row max only.
   static __device__ __forceinline__ void max_half(const char LDS_AS* stage, const Lane& ln, State& st, int kb,
-                                                  int key0, bool partial) {
-    st.mt = fmaxf(st.mt, row_max(scores(stage, ln, st, kb, key0, partial)));
+                                                  int key0, bool partial, bool low = false, float s_k = 0.0f) {
+    st.mt = fmaxf(st.mt, row_max(scores(stage, ln, st, kb, key0, partial, low, s_k)));
   }
 };
 
-template <int D, bool kOutBf16, bool kCausal>
+template <int D, bool kOutBf16, bool kCausal, bool kTiers>
 __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch a) {
-  using K = Kernel<D, kOutBf16, kCausal>;
+  using K = Kernel<D, kOutBf16, kCausal, kTiers>;
   using C = Cfg<D>;
   // two K/V stages
   __shared__ __attribute__((aligned(1024))) char smem_raw[2 * C::kStageBytes];
@@ -401,6 +470,28 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
     dma_source<D>((i * kWaves + wave) * 1024 + lane * 16, C::kVStride, row, chunk);
     ln.v_dma[i] = static_cast<uint32_t>(min(row, kHalf - 1) * vs_b) + chunk * 16;
   }
+
+  // tiered kernel: fp8 K rows of D bytes per (batch, KV head); the LOW test
+  // of key tile kt is q0 - (64 kt + 63) >= this head's boundary
+  const char* k8base = nullptr;
+  const float* k8scale = nullptr;
+  int low_dist = 0;
+  if constexpr (kTiers) {
+    const int64_t bg = static_cast<int64_t>(w.b) * a.sched.heads_kv + g;
+    k8base = static_cast<const char*>(a.k8) + bg * N * D;
+    k8scale = a.k8_scale + bg * ((N + kHalf - 1) / kHalf);
+    low_dist = a.head_low_dist[w.h];
+    ln.k8_rd = l32 * C::kK8Stride + ln.hi * 32;
+#pragma unroll
+    for (int i = 0; i < C::kK8BlocksPerWave; ++i) {
+      const int x = (i * kWaves + wave) * 1024 + lane * 16;
+      const int row = x / C::kK8Stride;
+      int chunk = (x - row * C::kK8Stride) / 16;
+      if (chunk >= D / 16) chunk = 0;  // row padding: re-read chunk 0 (never used)
+      ln.k8_dma[i] = static_cast<uint32_t>(min(row, kHalf - 1) * D + chunk * 16);
+    }
+  }
+  auto is_low = [&](int kt) -> bool { return kTiers && q0 - (kt * kBlockK + kBlockK - 1) >= low_dist; };
 
   // mask bounds of this lane's row: j <= hi_lim and (j < sink_lim or j >= win_lo);
   // per-head boundaries, when given, replace the layer's sink and window
@@ -463,6 +554,35 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
       st.q[q] = __builtin_bit_cast(bf16x8, x);
     }
   }
+  if constexpr (kTiers) {
+    // fp8 Q in the fp8 operand order: step q8 takes the bf16 k-steps
+    // 4 q8 .. 4 q8 + 3 of this lane (channels 16 s + 8 hi + 0..7), so the
+    // fp8 K rows are stored with the same channel order; scale = amax / 448
+    float amax = 0.0f;
+#pragma unroll
+    for (int q = 0; q < C::kQSteps; ++q)
+#pragma unroll
+      for (int x = 0; x < 8; ++x) amax = fmaxf(amax, fabsf(static_cast<float>(st.q[q][x])));
+    float p0, p1;
+    pair_halves(amax, p0, p1);
+    amax = fmaxf(p0, p1);
+    const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+    st.s_q = amax / 448.0f;
+#pragma unroll
+    for (int q8 = 0; q8 < C::kQ8Steps; ++q8)
+#pragma unroll
+      for (int qs = 0; qs < 4; ++qs)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          float v[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            v[x] = fminf(fmaxf(static_cast<float>(st.q[4 * q8 + qs][4 * half + x]) * inv, -448.0f), 448.0f);
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+          word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);
+          st.q8[q8][2 * qs + half] = word;
+        }
+  }
   st.m = -INFINITY;
   st.neg_mc = 0.0f;
   st.mt = -INFINITY;
@@ -475,9 +595,16 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
     // keys past the sequence end (the second half of a last tile can start
     // there) are outside the descriptor and land as zeros
     const int rows = max(N - key0, 0);
-    K::issue_dma(stage, ln, wave, buffer_rsrc(kbase + key0 * ks_b, static_cast<uint32_t>(rows * ks_b)),
-                 buffer_rsrc(vbase + key0 * vs_b, static_cast<uint32_t>(rows * vs_b)));
+    if (is_low(kt))
+      K::issue_dma_low(stage, ln, wave, buffer_rsrc(k8base + static_cast<int64_t>(key0) * D,
+                                                    static_cast<uint32_t>(rows * D)),
+                       buffer_rsrc(vbase + key0 * vs_b, static_cast<uint32_t>(rows * vs_b)));
+    else
+      K::issue_dma(stage, ln, wave, buffer_rsrc(kbase + key0 * ks_b, static_cast<uint32_t>(rows * ks_b)),
+                   buffer_rsrc(vbase + key0 * vs_b, static_cast<uint32_t>(rows * vs_b)));
   };
+  // scale of the fp8 K of the half starting at key0 (LOW halves only)
+  auto s_k_of = [&](int key0) -> float { return kTiers ? k8scale[key0 / kHalf] : 0.0f; };
 
   // Walks the kept tiles in 32-key halves, calling half(stage, key0, kb, partial).
   auto walk = [&](auto&& half) {
@@ -504,7 +631,10 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
     __syncthreads();  // all reads of the last stage are done before another walk refills it
   };
   auto attend = [&](const char LDS_AS* stage, int key0, int kb, bool partial) {
-    K::compute_half(stage, ln, st, kb, key0, partial, c_log2, need_ref);
+    const int kt = key0 / kBlockK;
+    const bool low = is_low(kt);
+    K::compute_half(stage, ln, st, kb, key0, partial, c_log2, need_ref, low,
+                    low ? s_k_of(key0 + kb * kHalf) : 0.0f);
   };
   auto clear = [&]() {
 #pragma unroll
@@ -523,7 +653,9 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
   walk(attend);
   if (__syncthreads_or(!(st.l <= kSumLimit))) {
     walk([&](const char LDS_AS* stage, int key0, int kb, bool partial) {
-      K::max_half(stage, ln, st, kb, key0, partial);
+      const int kt = key0 / kBlockK;
+      const bool low = is_low(kt);
+      K::max_half(stage, ln, st, kb, key0, partial, low, low ? s_k_of(key0 + kb * kHalf) : 0.0f);
     });
     st.m = st.mt;
     st.neg_mc = st.mt == -INFINITY ? 0.0f : -st.mt * c_log2;
@@ -561,9 +693,9 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
   }
 }
 
-template <int D, bool kOutBf16, bool kCausal>
+template <int D, bool kOutBf16, bool kCausal, bool kTiers = false>
 int launch_t(const AttnLaunch& a, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, kOutBf16, kCausal>),
+  hipLaunchKernelGGL((attn_fwd_kernel<D, kOutBf16, kCausal, kTiers>),
                      dim3(static_cast<unsigned>(a.sched.grid)), dim3(kThreads), 0, stream, a);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(TRI_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
@@ -572,6 +704,7 @@ int launch_t(const AttnLaunch& a, hipStream_t stream) {
 
 template <int D>
 int launch_d(const AttnLaunch& a, hipStream_t stream) {
+  if (a.k8) return a.o_bf16 ? launch_t<D, true, false, true>(a, stream) : launch_t<D, false, false, true>(a, stream);
   if (a.o_bf16) return a.causal ? launch_t<D, true, true>(a, stream) : launch_t<D, true, false>(a, stream);
   return a.causal ? launch_t<D, false, true>(a, stream) : launch_t<D, false, false>(a, stream);
 }

@@ -140,6 +140,12 @@ struct AttnLaunch {
   // per-head sink and window (device, [heads_q]), or NULL for the layer's
   const int32_t* head_sink;
   const int32_t* head_window;
+  // precision tiers (device; NULL k8 = off): fp8 K [B, Hkv, N, d bytes] in
+  // the fp8 operand channel order, its per-32-key scales [B, Hkv,
+  // ceil(N / 32)], and the per-head LOW boundary [heads_q]
+  const void* k8;
+  const float* k8_scale;
+  const int32_t* head_low_dist;
   Schedule sched;
 };
 
@@ -175,5 +181,19 @@ DynWorkspace dyn_workspace(int64_t batch, int64_t heads_q, int64_t heads_kv, int
 
 // Enqueue the four launches of the dynamic plan; returns TRI_OK or TRI_ERR_HIP.
 int launch_dyn_plan(const DynLaunch& a, void* stream);
+
+// ---------------------------------------------------------------- precision tiers
+
+struct QuantLaunch {
+  const void* k;  // bf16 [B, Hkv, N, d]
+  int64_t k_stride[3];
+  int32_t heads_kv, head_dim, seqlen;
+  int64_t n_blocks;  // batch * heads_kv * ceil(N / 32)
+  void* k8;          // out: fp8 [B, Hkv, N, d bytes]
+  float* scale;      // out: [B, Hkv, ceil(N / 32)]
+};
+
+// Enqueue the fp8 quantization of K; returns TRI_OK or TRI_ERR_HIP.
+int launch_quantize_k(const QuantLaunch& a, void* stream);
 
 }  // namespace triattn

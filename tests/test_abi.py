@@ -24,7 +24,8 @@ def test_header_symbols_are_exported():
     names = _declared_functions()
     assert {"tri_attn_plan", "tri_attn_prefill", "dense_causal_prefill",
             "tri_attn_last_error", "tri_dyn_plan_sizes", "tri_dyn_plan",
-            "tri_attn_prefill_lists", "tri_attn_plan_heads", "tri_attn_prefill_heads"} <= set(names)
+            "tri_attn_prefill_lists", "tri_attn_plan_heads", "tri_attn_prefill_heads",
+            "tri_attn_quantize_k_sizes", "tri_attn_quantize_k", "tri_attn_prefill_tiered"} <= set(names)
     lib = ctypes.CDLL(_abi.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n

@@ -1,0 +1,124 @@
+"""GPU parity of the precision tiers (TriAttention page: tiles scored at two
+precisions chosen by per-head diagonal-distance boundaries, combined in one
+normalised output; here fp8 e4m3 scores on far tiles): the fp8 copy of K
+bit for bit against the oracle's quantization, and the tiered layer against
+oracle/tiers.py, which scores far tiles from the same fp8 values."""
+import numpy as np
+import pytest
+import torch
+
+import static_triangle_sparse_amd as tsa
+import synth
+from oracle import tiers as otiers
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return gu.require_gpu()
+
+
+def _codes(values):
+    """e4m3 codes of values that are exactly e4m3 (the oracle's outputs).  A
+    zero maps to code 0: +0 and -0 (0x80) are the same value, and which of
+    the two a rounding to zero yields is not part of what the method fixes."""
+    table = otiers.e4m3_values()
+    pos = table[:127]                       # codes 0x00..0x7E, increasing
+    a = np.abs(values)
+    idx = np.searchsorted(pos, a)
+    assert np.all(pos[np.minimum(idx, 126)] == a), "not an e4m3 value"
+    return np.where((values < 0), idx | 0x80, idx).astype(np.uint8)
+
+
+def _permute_row(d):
+    """channel of byte p of a stored row (the kernel's operand order)"""
+    p = np.arange(d)
+    s, h, j = p // 64, (p // 32) % 2, p % 32
+    return 64 * s + 16 * (j // 8) + 8 * h + j % 8
+
+
+@pytest.mark.parametrize("N,d,B,Hkv", [(1000, 128, 1, 2), (333, 64, 2, 1)])
+def test_fp8_k_matches_the_oracle_quantization(dev, N, d, B, Hkv):
+    gu.note(f"fp8 K quantization N={N} d={d} B={B} Hkv={Hkv}")
+    bits, (q, k, v) = gu.make_inputs(60 + N, B, Hkv, Hkv, N, d, dev)
+    qk = tsa.quantize_k(q, k)
+    torch.cuda.synchronize()
+    kf = gu.as_f64(bits[1])
+    nh = -(-N // 32)
+    k8 = qk.k8[:B * Hkv * N * d].cpu().numpy().reshape(B, Hkv, N, d)
+    sc = qk.scale[:B * Hkv * nh].cpu().numpy().reshape(B, Hkv, nh)
+    perm = _permute_row(d)
+    for b in range(B):
+        for g in range(Hkv):
+            for hb in range(nh):
+                blk = kf[b, g, hb * 32:min(N, hb * 32 + 32)]
+                vals, s = otiers.quantize(blk)
+                assert sc[b, g, hb] == s, (b, g, hb)
+                want = _codes(vals)[:, perm]
+                got = k8[b, g, hb * 32:min(N, hb * 32 + 32)].copy()
+                got[got == 0x80] = 0
+                assert np.array_equal(got, want), (b, g, hb)
+
+
+CASES = [  # N, d, Hq, Hkv, sink, window, last_q, low_dist per head
+    (1000, 128, 4, 2, 64, 512, 64, [0, 128, 300, 10 ** 6]),
+    (700, 64, 2, 1, 32, 300, 0, [-63, 100]),
+    (129, 128, 2, 2, 16, 64, 32, [0, 0]),
+]
+
+
+@pytest.mark.parametrize("N,d,Hq,Hkv,sink,window,last_q,dist", CASES)
+def test_tiered_layer_matches_the_oracle(dev, N, d, Hq, Hkv, sink, window, last_q, dist):
+    gu.note(f"tiered layer N={N} d={d} Hq={Hq} dist={dist}")
+    bits, (q, k, v) = gu.make_inputs(70 + N, 1, Hq, Hkv, N, d, dev)
+    qk = tsa.quantize_k(q, k)
+    o = torch.full((1, Hq, N, d), float("nan"), dtype=torch.float32, device=dev)
+    lse = torch.full((1, Hq, N), float("nan"), dtype=torch.float32, device=dev)
+    tsa.prefill(q, k, v, mode="tiered", sink=sink, window=window, last_q=last_q, plan=qk,
+                low_dist=dist, o_dtype=torch.float32, out=o, lse=lse)
+    torch.cuda.synchronize()
+    qf, kf, vf = (gu.as_f64(x) for x in bits)
+    ro, rl = otiers.attention(qf, kf, vf, sink, window, last_q, dist)
+    err, rel = gu.check(o, lse, ro, rl, f"tiered N={N}")
+    gu.note(f"  max|dO|={err:.2e} max rel dLSE={rel:.2e}")
+
+
+def test_no_low_tiles_is_bit_identical_to_the_triangle_kernel(dev):
+    gu.note("tiered layer with boundaries past N vs tri_attn_prefill, N=1500")
+    N = 1500
+    _, (q, k, v) = gu.make_inputs(91, 1, 4, 2, N, 128, dev)
+    qk = tsa.quantize_k(q, k)
+    kw = dict(sink=64, window=256, last_q=64)
+    o = torch.empty((1, 4, N, 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((1, 4, N), dtype=torch.float32, device=dev)
+    tsa.prefill(q, k, v, mode="tiered", plan=qk, low_dist=[N + 1] * 4, o_dtype=torch.bfloat16,
+                out=o, lse=lse, **kw)
+    ot, lt = gu.run(q, k, v, "triangle", o_dtype=torch.bfloat16, **kw)
+    assert torch.equal(o, ot) and torch.equal(lse, lt)
+
+
+def test_llama_128k_tiered_sampled(dev):
+    # far tiles (distance >= 1024 keys) in fp8 on the 128K Llama-shaped layer
+    N, Hq, Hkv, d = 131072, 32, 8, 128
+    kw = dict(sink=128, window=2048, last_q=128)
+    gu.note("tiered 128K: inputs, quantize, layer")
+    bits, (q, k, v) = gu.make_inputs(0, 1, Hq, Hkv, N, d, dev)
+    qk = tsa.quantize_k(q, k)
+    o = torch.empty((1, Hq, N, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((1, Hq, N), dtype=torch.float32, device=dev)
+    tsa.prefill(q, k, v, mode="tiered", plan=qk, low_dist=[1024] * Hq, o_dtype=torch.bfloat16,
+                out=o, lse=lse, **kw)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    qf, kf, vf = (gu.as_f64(x) for x in bits)
+    rows = np.concatenate([np.arange(t * 128, (t + 1) * 128) for t in (0, 17, 500)] +
+                          [np.arange(N - 64, N)])
+    for h in (0, 13, 31):
+        g = h // 4
+        gu.note(f"  head {h}: oracle on {rows.size} rows")
+        ro, rl = otiers.attention(qf[:, h:h + 1], kf[:, g:g + 1], vf[:, g:g + 1], kw["sink"],
+                                  kw["window"], kw["last_q"], [1024], rows=rows)
+        idx = torch.from_numpy(rows).to(dev)
+        gu.check(o[:, h:h + 1][:, :, idx], lse[:, h:h + 1][:, :, idx], ro, rl, f"128K head {h}")
