@@ -308,10 +308,10 @@ def main(argv=None):
         print(f"[bench] dense causal: {dense_ms:.3f} ms/layer", file=sys.stderr, flush=True)
         if args.dyn_alpha > 0:
             extra["dynamic_dense"] = bench_dynamic(t, args, dense_ms, d, Hq, B, dev, stream)
-        if args.per_head:
-            extra["per_head_triangle"] = bench_per_head(t, args, cfg, d, Hq, B, dev, stream)
-        if args.low_dist >= 0:
-            extra["tiered_triangle"] = bench_tiered(t, args, cfg, plan, tri_ms, d, Hq, B, dev, stream)
+    if args.per_head:
+        extra["per_head_triangle"] = bench_per_head(t, args, cfg, d, Hq, B, dev, stream)
+    if args.low_dist >= 0:
+        extra["tiered_triangle"] = bench_tiered(t, args, cfg, plan, tri_ms, d, Hq, B, dev, stream)
 
     if args.calib_copy_mib:
         nbytes = args.calib_copy_mib << 20

@@ -276,11 +276,11 @@ struct Kernel {
   // lane; register r holds key key0 + 32 kb + 8 (r >> 2) + 4 hi + (r & 3).
   // Keys a PARTIAL tile drops are set to -inf.
   // In the tiered kernel a LOW half (low) is scored from fp8 K and Q with
-  // v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) and rescaled by
-  // s_q s_k (sqk) to raw score units.
+  // v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales); its scores are left
+  // in fp8 code units, s_q s_k times smaller than raw scores (the caller folds
+  // that factor into its exponent and maxima).
   static __device__ __forceinline__ f32x16 scores(const char LDS_AS* stage, const Lane& ln, const State& st,
-                                                  int kb, int key0, bool partial, bool low = false,
-                                                  float s_k = 0.0f) {
+                                                  int kb, int key0, bool partial, bool low = false) {
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.0f;
@@ -298,9 +298,6 @@ struct Kernel {
           s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, st.q8[q], s, 0, 0, 0, 0x7F7F7F7F, 0,
                                                               0x7F7F7F7F);
         }
-        const float f = st.s_q * s_k;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] *= f;
         done = true;
       }
     }
@@ -348,14 +345,16 @@ struct Kernel {
   // when a later key outscores the reference; the caller checks the row
   // sums at the end and, if any exceeds kSumLimit (so some P may have lost
   // range), reruns the list with each row's exact max as the reference.
+  // A LOW half's scores are sc times the fp8 code-unit scores (sc > 0).
   static __device__ __forceinline__ void compute_half(const char LDS_AS* stage, const Lane& ln,
                                                       State& st, int kb, int key0, bool partial,
                                                       float c_log2, bool& need_ref, bool low = false,
-                                                      float s_k = 0.0f) {
-    const f32x16 s = scores(stage, ln, st, kb, key0, partial, low, s_k);
+                                                      float sc = 1.0f) {
+    const f32x16 s = scores(stage, ln, st, kb, key0, partial, low);
+    const float c = low ? c_log2 * sc : c_log2;
     if (need_ref) {
       // a row with no kept key so far has O = 0 and l = 0: its reference may still move
-      const float mx = row_max(s);
+      const float mx = low ? row_max(s) * sc : row_max(s);
       if (st.m == -INFINITY && mx != -INFINITY) {
         st.m = mx;
         st.neg_mc = -mx * c_log2;
@@ -373,7 +372,7 @@ struct Kernel {
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kc * 8 + x], c_log2, st.neg_mc));
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kc * 8 + x], c, st.neg_mc));
         pf[kc * 8 + x] = p;
         pb[kc][x] = static_cast<__bf16>(p);
       }
@@ -414,8 +413,9 @@ struct Kernel {
 
   // Exact-max pass over one 32-key half: scores and row max only.
   static __device__ __forceinline__ void max_half(const char LDS_AS* stage, const Lane& ln, State& st, int kb,
-                                                  int key0, bool partial, bool low = false, float s_k = 0.0f) {
-    st.mt = fmaxf(st.mt, row_max(scores(stage, ln, st, kb, key0, partial, low, s_k)));
+                                                  int key0, bool partial, bool low = false, float sc = 1.0f) {
+    const float mx = row_max(scores(stage, ln, st, kb, key0, partial, low));
+    st.mt = fmaxf(st.mt, low ? mx * sc : mx);
   }
 };
 
@@ -543,7 +543,7 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
   };
 
   typename K::State st;
-  {
+  auto load_q = [&]() {
     const int qr = ln.qrow;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + w.b * a.q_stride[0] + w.h * a.q_stride[1] +
                          static_cast<int64_t>(qr) * a.q_stride[2] + ln.hi * 8;
@@ -553,36 +553,41 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
       if (qr < N) x = *reinterpret_cast<const u32x4*>(qp + q * 16);
       st.q[q] = __builtin_bit_cast(bf16x8, x);
     }
-  }
-  if constexpr (kTiers) {
-    // fp8 Q in the fp8 operand order: step q8 takes the bf16 k-steps
-    // 4 q8 .. 4 q8 + 3 of this lane (channels 16 s + 8 hi + 0..7), so the
-    // fp8 K rows are stored with the same channel order; scale = amax / 448
-    float amax = 0.0f;
+  };
+  // Tiered kernel: fp8 Q (from the bf16 Q just loaded) in the fp8 operand
+  // order: step q8 takes the bf16 k-steps 4 q8 .. 4 q8 + 3 of this lane
+  // (channels 16 s + 8 hi + 0..7), so the fp8 K rows are stored with the same
+  // channel order; scale = amax / 448.
+  auto make_q8 = [&]() {
+    if constexpr (kTiers) {
+      float amax = 0.0f;
 #pragma unroll
-    for (int q = 0; q < C::kQSteps; ++q)
+      for (int q = 0; q < C::kQSteps; ++q)
 #pragma unroll
-      for (int x = 0; x < 8; ++x) amax = fmaxf(amax, fabsf(static_cast<float>(st.q[q][x])));
-    float p0, p1;
-    pair_halves(amax, p0, p1);
-    amax = fmaxf(p0, p1);
-    const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
-    st.s_q = amax / 448.0f;
+        for (int x = 0; x < 8; ++x) amax = fmaxf(amax, fabsf(static_cast<float>(st.q[q][x])));
+      float p0, p1;
+      pair_halves(amax, p0, p1);
+      amax = fmaxf(p0, p1);
+      const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+      st.s_q = amax / 448.0f;
 #pragma unroll
-    for (int q8 = 0; q8 < C::kQ8Steps; ++q8)
+      for (int q8 = 0; q8 < C::kQ8Steps; ++q8)
 #pragma unroll
-      for (int qs = 0; qs < 4; ++qs)
+        for (int qs = 0; qs < 4; ++qs)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          float v[4];
+          for (int half = 0; half < 2; ++half) {
+            float v[4];
 #pragma unroll
-          for (int x = 0; x < 4; ++x)
-            v[x] = fminf(fmaxf(static_cast<float>(st.q[4 * q8 + qs][4 * half + x]) * inv, -448.0f), 448.0f);
-          int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-          word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);
-          st.q8[q8][2 * qs + half] = word;
-        }
-  }
+            for (int x = 0; x < 4; ++x)
+              v[x] = fminf(fmaxf(static_cast<float>(st.q[4 * q8 + qs][4 * half + x]) * inv, -448.0f), 448.0f);
+            int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+            word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);
+            st.q8[q8][2 * qs + half] = word;
+          }
+    }
+  };
+  load_q();
+  make_q8();
   st.m = -INFINITY;
   st.neg_mc = 0.0f;
   st.mt = -INFINITY;
@@ -590,12 +595,13 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
 
   const float c_log2 = a.scale * kLog2e;
 
-  auto dma = [&](char LDS_AS* stage, int kt, int kb) {
+  // copies of half kb of tile kt into a stage: bf16 K (high) or fp8 K (LOW), and V
+  auto dma = [&](char LDS_AS* stage, int kt, int kb, bool low) {
     const int key0 = kt * kBlockK + kb * kHalf;
     // keys past the sequence end (the second half of a last tile can start
     // there) are outside the descriptor and land as zeros
     const int rows = max(N - key0, 0);
-    if (is_low(kt))
+    if (kTiers && low)
       K::issue_dma_low(stage, ln, wave, buffer_rsrc(k8base + static_cast<int64_t>(key0) * D,
                                                     static_cast<uint32_t>(rows * D)),
                        buffer_rsrc(vbase + key0 * vs_b, static_cast<uint32_t>(rows * vs_b)));
@@ -603,38 +609,66 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
       K::issue_dma(stage, ln, wave, buffer_rsrc(kbase + key0 * ks_b, static_cast<uint32_t>(rows * ks_b)),
                    buffer_rsrc(vbase + key0 * vs_b, static_cast<uint32_t>(rows * vs_b)));
   };
-  // scale of the fp8 K of the half starting at key0 (LOW halves only)
-  auto s_k_of = [&](int key0) -> float { return kTiers ? k8scale[key0 / kHalf] : 0.0f; };
 
-  // Walks the kept tiles in 32-key halves, calling half(stage, key0, kb, partial).
-  auto walk = [&](auto&& half) {
-    load_list(e_begin);
-    if (e_begin < e_end) dma(smem, tile_of(e_begin), 0);
-    int cur = 0;  // byte offset of the stage holding the current half
-    for (int e = e_begin; e < e_end; ++e) {
-      const int kt = tile_of(e);
-      const bool partial = partial_of(e, kt);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        wait_vmcnt0();    // this wave's copies of this half have landed
-        __syncthreads();  // ... and every wave's; all reads of the other stage are done
-        if (kb == 0) {
-          dma(smem + (cur ^ C::kStageBytes), kt, 1);
-        } else if (e + 1 < e_end) {
-          if (e + 1 - list_e0 == 64) load_list(e + 1);
-          dma(smem + (cur ^ C::kStageBytes), tile_of(e + 1), 0);
-        }
-        half(smem + cur, kt * kBlockK, kb, partial);
-        cur ^= C::kStageBytes;
-      }
+  // The LOW test is monotone in kt, so in an ascending list the LOW tiles
+  // are the entries [e_begin, e_split); the tiered walk takes them first with
+  // fp8 Q only, then reloads bf16 Q for the rest, so the two copies of Q are
+  // never held together.
+  int e_split = e_begin;
+  if constexpr (kTiers) {
+    for (int e0 = e_begin; e0 < e_end; e0 += 64) {
+      const int e = e0 + lane;
+      const uint64_t bits = __ballot(e < e_end && is_low(a.k_tile[e]));
+      e_split += __popcll(bits);
+      if (~bits != 0) break;
     }
+  }
+
+  // Walks the kept tiles in 32-key halves: entries [e_begin, e_split) with
+  // low_half, then at_split(), then [e_split, e_end) with high_half; each half
+  // callback is called as half(stage, key0, kb, partial).
+  auto walk = [&](auto&& low_half, auto&& at_split, auto&& high_half) {
+    load_list(e_begin);
+    if (e_begin < e_end) dma(smem, tile_of(e_begin), 0, e_begin < e_split);
+    int cur = 0;  // byte offset of the stage holding the current half
+    auto run = [&](int e_lo, int e_hi, bool low, auto&& half) {
+      for (int e = e_lo; e < e_hi; ++e) {
+        const int kt = tile_of(e);
+        const bool partial = partial_of(e, kt);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          wait_vmcnt0();    // this wave's copies of this half have landed
+          __syncthreads();  // ... and every wave's; all reads of the other stage are done
+          if (kb == 0) {
+            dma(smem + (cur ^ C::kStageBytes), kt, 1, low);
+          } else if (e + 1 < e_end) {
+            if (e + 1 - list_e0 == 64) load_list(e + 1);
+            dma(smem + (cur ^ C::kStageBytes), tile_of(e + 1), 0, low && e + 1 < e_split);
+          }
+          half(smem + cur, kt * kBlockK, kb, partial);
+          cur ^= C::kStageBytes;
+        }
+      }
+    };
+    if constexpr (kTiers) {
+      run(e_begin, e_split, true, low_half);
+      at_split();
+    }
+    run(e_split, e_end, false, high_half);
     __syncthreads();  // all reads of the last stage are done before another walk refills it
   };
+  // score scale of the LOW half starting at key0: s_q times the fp8 K scale
+  // of that half (kept positive so that 0 * -inf never arises: a zero scale
+  // means all-zero codes, whose scores are 0 at any positive scale)
+  auto low_sc = [&](int key0) -> float {
+    if constexpr (kTiers) return fmaxf(st.s_q * k8scale[key0 / kHalf], 1.17549435e-38f);
+    return 1.0f;
+  };
+  auto attend_low = [&](const char LDS_AS* stage, int key0, int kb, bool partial) {
+    K::compute_half(stage, ln, st, kb, key0, partial, c_log2, need_ref, true, low_sc(key0 + kb * kHalf));
+  };
   auto attend = [&](const char LDS_AS* stage, int key0, int kb, bool partial) {
-    const int kt = key0 / kBlockK;
-    const bool low = is_low(kt);
-    K::compute_half(stage, ln, st, kb, key0, partial, c_log2, need_ref, low,
-                    low ? s_k_of(key0 + kb * kHalf) : 0.0f);
+    K::compute_half(stage, ln, st, kb, key0, partial, c_log2, need_ref);
   };
   auto clear = [&]() {
 #pragma unroll
@@ -644,24 +678,37 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
     st.l = 0.0f;
     st.lb = 0.0f;
   };
+  auto reload_q = [&]() {
+    if constexpr (kTiers) load_q();
+  };
+  auto requant_q = [&]() {
+    if constexpr (kTiers) {
+      load_q();
+      make_q8();
+    }
+  };
 
   // Usual case: one walk with a fixed reference per row.  Every P of a row is
   // at most its row sum, so below kSumLimit nothing lost range; otherwise
   // walk again for the exact row maxima and once more with them as the
   // reference (then every P <= 1).
   clear();
-  walk(attend);
+  walk(attend_low, reload_q, attend);
   if (__syncthreads_or(!(st.l <= kSumLimit))) {
+    requant_q();
     walk([&](const char LDS_AS* stage, int key0, int kb, bool partial) {
-      const int kt = key0 / kBlockK;
-      const bool low = is_low(kt);
-      K::max_half(stage, ln, st, kb, key0, partial, low, low ? s_k_of(key0 + kb * kHalf) : 0.0f);
-    });
+           K::max_half(stage, ln, st, kb, key0, partial, true, low_sc(key0 + kb * kHalf));
+         },
+         reload_q,
+         [&](const char LDS_AS* stage, int key0, int kb, bool partial) {
+           K::max_half(stage, ln, st, kb, key0, partial);
+         });
     st.m = st.mt;
     st.neg_mc = st.mt == -INFINITY ? 0.0f : -st.mt * c_log2;
     need_ref = false;
     clear();
-    walk(attend);
+    requant_q();
+    walk(attend_low, reload_q, attend);
   }
 
   // epilogue
