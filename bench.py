@@ -119,6 +119,64 @@ def time_launches(fn, steps, warmup):
     return start.elapsed_time(stop) / steps, wall
 
 
+def time_each(fn, runs, flush_mib=0):
+    """Per-launch ms of `runs` launches of fn(), each bracketed by its own HIP
+    events on the launch stream.  With flush_mib, a write of that many MiB of
+    scratch precedes every launch (outside the events), so each launch starts
+    with K/V/Q evicted from the 256 MB Infinity Cache and the L2s."""
+    import torch
+    scratch = torch.empty(max(1, flush_mib) << 20, dtype=torch.uint8, device="cuda") if flush_mib else None
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(runs)]
+    for i, (a, b) in enumerate(ev):
+        if scratch is not None:
+            scratch.fill_(i & 0xFF)
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    del scratch
+    return {"median_ms": round(ms[len(ms) // 2], 4), "min_ms": round(ms[0], 4), "runs": runs}
+
+
+def measure_clock(fn, launch_ms, seconds=2.5, skip_s=1.0):
+    """Mean shader clock (MHz) of GPU 0 while fn() runs back to back for about
+    `seconds`: the launches are queued, then amdsmi's per-XCD graphics clocks
+    are read every 0.25 s once `skip_s` of ramp-up has passed (amdsmi refreshes
+    its metrics about once a second).  Returns (mhz or None, detail)."""
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handles = amdsmi.amdsmi_get_processor_handles()
+        if len(handles) != 1:
+            return None, f"{len(handles)} GPUs visible to amdsmi"
+        h = handles[0]
+
+        def read():
+            m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+            xcd = [float(x) for x in m.get("current_gfxclks", []) if isinstance(x, (int, float))]
+            if xcd:
+                return sum(xcd) / len(xcd)
+            return float(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"])
+        read()
+    except Exception as e:  # noqa: BLE001 - report, never fail the bench over it
+        return None, f"amdsmi: {type(e).__name__}: {e}"
+    n = max(1, int(seconds * 1e3 / max(launch_ms, 1e-3)))
+    t0 = time.perf_counter()
+    for _ in range(n):
+        fn()
+    samples = []
+    while time.perf_counter() - t0 < seconds:
+        time.sleep(0.25)
+        if time.perf_counter() - t0 >= skip_s:
+            samples.append(read())
+    torch.cuda.synchronize()
+    if not samples:
+        return None, "no samples"
+    return sum(samples) / len(samples), f"{len(samples)} samples over {n} launches (mean of the XCD clocks)"
+
+
 def cpu_baseline(bits, cfg, plan, n_random_tiles=128):
     """The fp64 oracle, as it stands, on a bounded sample of the same layer:
     query tiles {0, 1, 15, 16, 17, nq-2, nq-1} plus `n_random_tiles` seeded
@@ -294,6 +352,19 @@ def main(argv=None):
     tiles = kept_tiles_per_head(plan)
     flops = 4.0 * 128 * 64 * d * tiles * Hq * B
     tflops = flops / (tri_ms * 1e-3) / 1e12
+    # per-launch spread, warm (back to back) and cold (caches flushed by a 512 MiB write)
+    runs = {"warm": time_each(tri, max(20, args.steps)), "cold": time_each(tri, max(20, args.steps), 512)}
+    runs["cold"]["flush"] = "512 MiB device write before each launch, outside the events"
+    print(f"[bench] triangle per launch: warm median {runs['warm']['median_ms']:.3f} ms, cold median "
+          f"{runs['cold']['median_ms']:.3f} ms", file=sys.stderr, flush=True)
+    # the same launches for ~2.5 s more, with the shader clock read meanwhile:
+    # the fraction of the MFMA peak at the clock the chip actually ran
+    sclk, detail = measure_clock(tri, tri_ms)
+    at_clock = {"sclk_mhz": round(sclk, 1) if sclk else None, "how": detail}
+    if sclk:
+        peak_at = 256 * 4096 * sclk * 1e6 / 1e12
+        at_clock.update(peak_tflops_at_sclk=round(peak_at, 1), pct_peak_at_sclk=round(100 * tflops / peak_at, 2))
+    print(f"[bench] shader clock: {at_clock}", file=sys.stderr, flush=True)
 
     extra = {}
     if not args.no_dense:
@@ -349,6 +420,8 @@ def main(argv=None):
                    "o_dtype": "bf16", "kept_tiles_per_head": tiles},
         "triangle_ms": round(tri_ms, 4),
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "triangle_per_launch": runs,
+        "measured_clock": at_clock,
         **extra,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
