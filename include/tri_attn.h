@@ -263,6 +263,37 @@ int tri_attn_prefill_tiered(const tri_attn_tensors* t, const tri_mask_params* mp
                             const int32_t* d_row_ptr, const int32_t* d_k_tile,
                             const uint8_t* d_flags, void* stream);
 
+/*
+ * Split of the last-Q rows.  Query tiles holding last-Q rows keep every key
+ * tile (2048 at N = 131072 against ~38 for a band tile), and one workgroup
+ * walking such a list sets the layer's critical path when the band is short.
+ * The split launch walks each of those lists in chunks of chunk_tiles key
+ * tiles on separate workgroups, each leaving an unnormalised partial output
+ * and its row statistics in a caller-provided workspace, then merges the
+ * chunks by the usual rescaling of partial softmax sums.  The layer computed
+ * is the triangle layer of tri_attn_prefill (TriangleMix pages: sink, window
+ * and last-Q regions), or of tri_attn_prefill_heads when per-head boundaries
+ * are given; only the summation order of the split rows differs.
+ *
+ * tri_attn_split_workspace_size -- device bytes the split launch needs for
+ * (t, mp, chunk_tiles): 0 when mp has no last-Q rows (last_q = 0).
+ * mp->kind must be TRI_MASK_TRIANGLE; chunk_tiles >= 1.
+ * tri_attn_prefill_split -- enqueue the split layer on the plan arrays of
+ * tri_attn_plan (d_head_sink = d_head_window = NULL) or of
+ * tri_attn_plan_heads (device int32 [heads_q] boundaries, as for
+ * tri_attn_prefill_heads).  d_workspace: device, 256-byte aligned, at least
+ * the size above (TRI_ERR_CAPACITY otherwise); its contents need no
+ * initialisation and are overwritten.  Two launches (attention, then merge)
+ * on `stream`; calls that share a workspace must not overlap.
+ */
+int tri_attn_split_workspace_size(const tri_attn_tensors* t, const tri_mask_params* mp,
+                                  int32_t chunk_tiles, int64_t* bytes);
+int tri_attn_prefill_split(const tri_attn_tensors* t, const tri_mask_params* mp,
+                           const int32_t* d_head_sink, const int32_t* d_head_window,
+                           const int32_t* d_row_ptr, const int32_t* d_k_tile,
+                           const uint8_t* d_flags, int32_t chunk_tiles, void* d_workspace,
+                           int64_t workspace_bytes, void* stream);
+
 /* Message for the last non-OK return on this thread ("" if none). */
 const char* tri_attn_last_error(void);
 
@@ -280,6 +311,15 @@ int tri_attn_work_item(int32_t batch, int32_t heads_q, int32_t heads_kv,
                        int64_t seqlen, int32_t kind, int64_t last_q, int64_t bid,
                        int32_t* b_out, int32_t* h_out, int32_t* qtile_out,
                        int64_t* grid_out);
+
+/*
+ * tri_attn_split_work_item -- the same view for a split triangle launch:
+ * also writes the chunk (or -1 for a whole row) the block computes.
+ */
+int tri_attn_split_work_item(int32_t batch, int32_t heads_q, int32_t heads_kv, int64_t seqlen,
+                             int64_t last_q, int32_t chunk_tiles, int64_t bid, int32_t* b_out,
+                             int32_t* h_out, int32_t* qtile_out, int32_t* chunk_out,
+                             int64_t* grid_out);
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,8 @@ from ._abi import (  # noqa: F401
     tri_attn_abi_version, tri_attn_plan, tri_attn_plan_heads, tri_attn_prefill,
     tri_attn_prefill_heads, tri_attn_prefill_lists, tri_attn_prefill_tiered,
     tri_attn_quantize_k, tri_attn_quantize_k_sizes, tri_attn_work_item, tri_dyn_plan,
-    tri_dyn_plan_sizes,
+    tri_dyn_plan_sizes, tri_attn_prefill_split, tri_attn_split_work_item,
+    tri_attn_split_workspace_size,
 )
 
 __all__ = [
@@ -35,7 +36,24 @@ __all__ = [
     "DynPlan", "dyn_plan", "tri_dyn_plan", "tri_dyn_plan_sizes", "tri_attn_prefill_lists",
     "HeadPlan", "head_plan", "tri_attn_plan_heads", "tri_attn_prefill_heads",
     "QuantizedK", "quantize_k", "tri_attn_quantize_k", "tri_attn_prefill_tiered",
+    "split_workspace", "tri_attn_prefill_split", "tri_attn_split_workspace_size",
 ]
+
+_WORKSPACE = {}
+
+
+def split_workspace(nbytes: int, device):
+    """A device workspace of at least ``nbytes`` for split launches, kept for
+    the life of the process (one per device, grown on demand), so that it
+    outlives every launch enqueued with it."""
+    import torch
+    key = str(device)
+    ws = _WORKSPACE.get(key)
+    if ws is None or ws.numel() < nbytes:
+        # torch's caching allocator returns 512-byte-aligned blocks
+        ws = torch.empty(max(256, nbytes), dtype=torch.uint8, device=device)
+        _WORKSPACE[key] = ws
+    return ws
 
 
 def layer_mode(layer: int, tri_start: int) -> str:
@@ -189,10 +207,13 @@ def dyn_plan(q, k, alpha, scale=None, stream=None) -> DynPlan:
 
 
 def prefill(q, k, v, mode="triangle", sink=0, window=1, last_q=0, o_dtype=None, scale=None,
-            out=None, lse=None, stream=None, plan=None, low_dist=None):
+            out=None, lse=None, stream=None, plan=None, low_dist=None, split=None):
     """One attention layer on the GPU; returns (o, lse).  ``mode`` is
-    "triangle" (planned tile list), "causal" (dense layer) or "lists"
-    (per-head tile lists of a DynPlan, causal mask inside the tiles)."""
+    "triangle" (planned tile list), "triangle_heads" (a HeadPlan), "tiered"
+    (fp8 far tiles), "causal" (dense layer) or "lists" (per-head tile lists
+    of a DynPlan, causal mask inside the tiles).  ``split``: for "triangle" and
+    "triangle_heads", walk the last-Q rows in chunks of this many key tiles on
+    separate workgroups (tri_attn_prefill_split)."""
     import torch
     B, Hq, N, d = q.shape
     if o_dtype is None:
@@ -203,7 +224,23 @@ def prefill(q, k, v, mode="triangle", sink=0, window=1, last_q=0, o_dtype=None, 
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     t = make_tensors(q, k, v, out, lse, scale)
     s = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
-    if mode == "causal":
+    if split is not None and mode not in ("triangle", "triangle_heads"):
+        raise ValueError("split= applies to modes 'triangle' and 'triangle_heads'")
+    if split is not None:
+        if mode == "triangle":
+            p = device_plan(N, "triangle", sink, window, last_q, q.device)
+            heads = (None, None)
+        else:
+            if plan is None:
+                raise ValueError("mode 'triangle_heads' needs plan= (a HeadPlan)")
+            p = plan
+            heads = (plan.d_sink.data_ptr(), plan.d_window.data_ptr())
+        nbytes = tri_attn_split_workspace_size(t, p.mp, int(split))
+        ws = split_workspace(nbytes, q.device)
+        tri_attn_prefill_split(t, p.mp, heads[0], heads[1], p.d_row_ptr.data_ptr(),
+                               p.d_k_tile.data_ptr(), p.d_flags.data_ptr(), int(split), ws.data_ptr(),
+                               ws.numel(), s)
+    elif mode == "causal":
         dense_causal_prefill(t, s)
     elif mode == "triangle":
         p = device_plan(N, "triangle", sink, window, last_q, q.device)

@@ -144,6 +144,19 @@ def load() -> ctypes.CDLL:
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.tri_attn_prefill_tiered.restype = ctypes.c_int
+    lib.tri_attn_split_workspace_size.argtypes = [P(AttnTensors), P(MaskParams), ctypes.c_int32,
+                                                  P(ctypes.c_int64)]
+    lib.tri_attn_split_workspace_size.restype = ctypes.c_int
+    lib.tri_attn_prefill_split.argtypes = [P(AttnTensors), P(MaskParams), ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                           ctypes.c_int64, ctypes.c_void_p]
+    lib.tri_attn_prefill_split.restype = ctypes.c_int
+    lib.tri_attn_split_work_item.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                             ctypes.c_int64, P(ctypes.c_int32), P(ctypes.c_int32),
+                                             P(ctypes.c_int32), P(ctypes.c_int32), P(ctypes.c_int64)]
+    lib.tri_attn_split_work_item.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -290,3 +303,31 @@ def tri_attn_prefill_tiered(t: AttnTensors, mp: MaskParams, d_low_dist: int, d_k
     """Enqueue a triangle layer with fp8 scores on far tiles (device pointers)."""
     _check(load().tri_attn_prefill_tiered(ctypes.byref(t), ctypes.byref(mp), d_low_dist, d_k8,
                                           d_scale, d_row_ptr, d_k_tile, d_flags, stream))
+
+
+def tri_attn_split_workspace_size(t: AttnTensors, mp: MaskParams, chunk_tiles: int) -> int:
+    """Device bytes of the workspace of a split launch (0: nothing to split)."""
+    n = ctypes.c_int64()
+    _check(load().tri_attn_split_workspace_size(ctypes.byref(t), ctypes.byref(mp), chunk_tiles,
+                                                ctypes.byref(n)))
+    return n.value
+
+
+def tri_attn_prefill_split(t: AttnTensors, mp: MaskParams, d_head_sink, d_head_window, d_row_ptr: int,
+                           d_k_tile: int, d_flags: int, chunk_tiles: int, d_workspace, workspace_bytes: int,
+                           stream: int) -> None:
+    """Enqueue a triangle layer whose last-Q rows are walked in chunks (device
+    pointers; head arrays None for one shared plan)."""
+    _check(load().tri_attn_prefill_split(ctypes.byref(t), ctypes.byref(mp), d_head_sink, d_head_window,
+                                         d_row_ptr, d_k_tile, d_flags, chunk_tiles, d_workspace,
+                                         workspace_bytes, stream))
+
+
+def tri_attn_split_work_item(batch, heads_q, heads_kv, seqlen, last_q, chunk_tiles, bid):
+    """(b, h, qtile, chunk, grid) of block ``bid`` of a split launch."""
+    b, h, t, c = (ctypes.c_int32() for _ in range(4))
+    grid = ctypes.c_int64()
+    _check(load().tri_attn_split_work_item(batch, heads_q, heads_kv, seqlen, last_q, chunk_tiles, bid,
+                                           ctypes.byref(b), ctypes.byref(h), ctypes.byref(t),
+                                           ctypes.byref(c), ctypes.byref(grid)))
+    return b.value, h.value, t.value, c.value, grid.value

@@ -48,7 +48,8 @@ def build(verbose: bool = False, lib_path: str = LIB, kernel_src: str = None,
         objs.append(obj)
     for name, src in (("attn_fwd_gfx950", kernel_src or os.path.join(CSRC, "attn_fwd_gfx950.hip")),
                       ("dyn_select_gfx950", os.path.join(CSRC, "dyn_select_gfx950.hip")),
-                      ("tiers_gfx950", os.path.join(CSRC, "tiers_gfx950.hip"))):
+                      ("tiers_gfx950", os.path.join(CSRC, "tiers_gfx950.hip")),
+                      ("split_gfx950", os.path.join(CSRC, "split_gfx950.hip"))):
         kobj = os.path.join(build_dir, name + ".o")
         out = _run([hipcc, *HIPCC_FLAGS, *extra_hipcc_flags, "-I", INCLUDE, "-I", CSRC, "-c", src,
                     "-o", kobj])

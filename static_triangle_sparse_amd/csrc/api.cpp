@@ -124,7 +124,25 @@ int64_t causal_tiles(int64_t N) {
   return n;
 }
 
+// Heavy tiles and chunks of a split launch of a triangle plan.
+void split_shape(int64_t N, int64_t last_q, int32_t chunk_tiles, int32_t* n_heavy, int32_t* n_split) {
+  const Schedule s = make_schedule(1, 1, 1, N, TRI_KERNEL_BLOCK_Q, false, std::min(last_q, N));
+  const int64_t nkt = (N + TRI_KERNEL_BLOCK_K - 1) / TRI_KERNEL_BLOCK_K;
+  *n_heavy = s.n_heavy;
+  *n_split = s.n_heavy > 0 ? static_cast<int32_t>((nkt + chunk_tiles - 1) / chunk_tiles) : 1;
+}
+
 }  // namespace
+
+SplitWorkspace split_workspace(int64_t batch, int64_t heads_q, int64_t head_dim, int64_t n_heavy,
+                               int64_t n_split) {
+  SplitWorkspace w{};
+  w.n_items = n_split > 1 ? batch * heads_q * n_heavy * n_split : 0;
+  w.stats = 0;
+  w.o = align256(w.n_items * 3 * TRI_KERNEL_BLOCK_Q * 4);
+  w.total = w.o + align256(w.n_items * TRI_KERNEL_BLOCK_Q * head_dim * 4);
+  return w;
+}
 
 DynWorkspace dyn_workspace(int64_t batch, int64_t heads_q, int64_t heads_kv, int64_t head_dim,
                            int64_t seqlen) {
@@ -340,6 +358,106 @@ extern "C" int tri_attn_prefill_heads(const tri_attn_tensors* t, const tri_mask_
   a.head_sink = d_head_sink;
   a.head_window = d_head_window;
   return launch_attn_fwd(a, stream);
+}
+
+extern "C" int tri_attn_split_workspace_size(const tri_attn_tensors* t, const tri_mask_params* mp,
+                                             int32_t chunk_tiles, int64_t* bytes) {
+  clear_error();
+  int st = validate_mask(mp);
+  if (st != TRI_OK) return st;
+  if ((st = validate_tensors(t)) != TRI_OK) return st;
+  if (!bytes) return fail(TRI_ERR_INVALID, "bytes must be non-NULL");
+  if (mp->kind != TRI_MASK_TRIANGLE) return fail(TRI_ERR_INVALID, "the split applies to the triangle mask");
+  if (chunk_tiles < 1) return fail(TRI_ERR_INVALID, "chunk_tiles must be >= 1");
+  if (mp->seqlen != t->seqlen)
+    return fail(TRI_ERR_INVALID, "mask seqlen %lld differs from tensor seqlen %lld",
+                static_cast<long long>(mp->seqlen), static_cast<long long>(t->seqlen));
+  int32_t n_heavy = 0, n_split = 1;
+  if (t->seqlen > 0) split_shape(t->seqlen, mp->last_q, chunk_tiles, &n_heavy, &n_split);
+  *bytes = split_workspace(t->batch, t->heads_q, t->head_dim, n_heavy, n_split).total;
+  return TRI_OK;
+}
+
+extern "C" int tri_attn_prefill_split(const tri_attn_tensors* t, const tri_mask_params* mp,
+                                      const int32_t* d_head_sink, const int32_t* d_head_window,
+                                      const int32_t* d_row_ptr, const int32_t* d_k_tile,
+                                      const uint8_t* d_flags, int32_t chunk_tiles, void* d_workspace,
+                                      int64_t workspace_bytes, void* stream) {
+  clear_error();
+  int st = validate_mask(mp);
+  if (st != TRI_OK) return st;
+  if ((st = validate_tensors(t)) != TRI_OK) return st;
+  if (mp->kind != TRI_MASK_TRIANGLE) return fail(TRI_ERR_INVALID, "the split applies to the triangle mask");
+  if (mp->block_q != TRI_KERNEL_BLOCK_Q || mp->block_k != TRI_KERNEL_BLOCK_K)
+    return fail(TRI_ERR_UNSUPPORTED, "the kernel walks %dx%d tiles; plan has %dx%d",
+                TRI_KERNEL_BLOCK_Q, TRI_KERNEL_BLOCK_K, mp->block_q, mp->block_k);
+  if (mp->seqlen != t->seqlen)
+    return fail(TRI_ERR_INVALID, "mask seqlen %lld differs from tensor seqlen %lld",
+                static_cast<long long>(mp->seqlen), static_cast<long long>(t->seqlen));
+  if (chunk_tiles < 1) return fail(TRI_ERR_INVALID, "chunk_tiles must be >= 1");
+  if ((d_head_sink == nullptr) != (d_head_window == nullptr))
+    return fail(TRI_ERR_INVALID, "per-head sink and window go together (both NULL for one plan)");
+  if (!d_row_ptr || !d_k_tile || !d_flags)
+    return fail(TRI_ERR_INVALID, "plan arrays (row_ptr, k_tile, flags) must be non-NULL");
+  if (!aligned(d_row_ptr, 4) || !aligned(d_k_tile, 4) || (d_head_sink && !aligned(d_head_sink, 4)) ||
+      (d_head_window && !aligned(d_head_window, 4)))
+    return fail(TRI_ERR_INVALID, "int32 arrays must be 4-byte aligned");
+  if (t->seqlen == 0) return TRI_OK;
+  int32_t n_heavy = 0, n_split = 1;
+  split_shape(t->seqlen, mp->last_q, chunk_tiles, &n_heavy, &n_split);
+  const SplitWorkspace ws = split_workspace(t->batch, t->heads_q, t->head_dim, n_heavy, n_split);
+  if (ws.total > 0) {
+    if (!d_workspace || !aligned(d_workspace, 256))
+      return fail(TRI_ERR_INVALID, "workspace must be non-NULL and 256-byte aligned");
+    if (workspace_bytes < ws.total)
+      return fail(TRI_ERR_CAPACITY, "workspace of %lld bytes, %lld needed",
+                  static_cast<long long>(workspace_bytes), static_cast<long long>(ws.total));
+  }
+  const int64_t nq = (t->seqlen + TRI_KERNEL_BLOCK_Q - 1) / TRI_KERNEL_BLOCK_Q;
+  AttnLaunch a = make_launch(t, false, mp->sink, mp->window, mp->last_q);
+  a.sched = make_schedule(t->batch, t->heads_q, t->heads_kv, t->seqlen, TRI_KERNEL_BLOCK_Q, false, a.last_q,
+                          n_split);
+  a.row_ptr = d_row_ptr;
+  a.k_tile = d_k_tile;
+  a.flags = d_flags;
+  if (d_head_sink) {
+    a.list_batch_rows = 0;
+    a.list_head_rows = static_cast<int32_t>(nq);
+    a.head_sink = d_head_sink;
+    a.head_window = d_head_window;
+  }
+  a.chunk_tiles = chunk_tiles;
+  if (ws.total > 0) {
+    a.split_stats = reinterpret_cast<float*>(static_cast<char*>(d_workspace) + ws.stats);
+    a.split_o = reinterpret_cast<float*>(static_cast<char*>(d_workspace) + ws.o);
+  }
+  if ((st = launch_attn_fwd(a, stream)) != TRI_OK) return st;
+  return launch_split_merge(a, stream);
+}
+
+extern "C" int tri_attn_split_work_item(int32_t batch, int32_t heads_q, int32_t heads_kv, int64_t seqlen,
+                                        int64_t last_q, int32_t chunk_tiles, int64_t bid, int32_t* b_out,
+                                        int32_t* h_out, int32_t* qtile_out, int32_t* chunk_out,
+                                        int64_t* grid_out) {
+  clear_error();
+  if (!b_out || !h_out || !qtile_out || !chunk_out || !grid_out)
+    return fail(TRI_ERR_INVALID, "output pointers must be non-NULL");
+  if (batch < 1 || heads_q < 1 || heads_kv < 1 || heads_q % heads_kv)
+    return fail(TRI_ERR_INVALID, "bad head counts");
+  if (seqlen < 1 || seqlen >= kMaxSeqlen) return fail(TRI_ERR_INVALID, "bad seqlen");
+  if (last_q < 0) return fail(TRI_ERR_INVALID, "last_q must be >= 0");
+  if (chunk_tiles < 1) return fail(TRI_ERR_INVALID, "chunk_tiles must be >= 1");
+  int32_t n_heavy = 0, n_split = 1;
+  split_shape(seqlen, last_q, chunk_tiles, &n_heavy, &n_split);
+  const Schedule s = make_schedule(batch, heads_q, heads_kv, seqlen, TRI_KERNEL_BLOCK_Q, false,
+                                   std::min(last_q, seqlen), n_split);
+  const WorkItem w = schedule_item(s, bid);
+  *b_out = w.b;
+  *h_out = w.h;
+  *qtile_out = w.t;
+  *chunk_out = w.c;
+  *grid_out = s.grid;
+  return TRI_OK;
 }
 
 extern "C" int tri_attn_quantize_k_sizes(const tri_attn_tensors* t, int64_t* k8_bytes,

@@ -519,6 +519,12 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
     const int64_t r = w.b * a.list_batch_rows + static_cast<int64_t>(w.h) * a.list_head_rows + w.t;
     e_begin = a.row_ptr[r];
     e_end = a.row_ptr[r + 1];
+    if (!kTiers && w.c >= 0) {
+      // chunk c of a split row: entries [c C, (c + 1) C) of the list (possibly none)
+      const int lo = e_begin + w.c * a.chunk_tiles;
+      e_end = min(e_end, lo + a.chunk_tiles);
+      e_begin = min(lo, e_end);
+    }
   }
   // tile list in registers, 64 entries per batch (lane i holds entry e0 + i)
   int list_e0 = e_begin;
@@ -716,6 +722,31 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
   pair_halves(st.l, l0, l1);
   pair_halves(st.lb, b0, b1);
   const float l_tot = l0 + l1;
+  if (!kTiers && w.c >= 0) {
+    // chunk of a split row (the tiered kernel is never split): unnormalised O and the row's (reference max, fp32
+    // sum, bf16 sum), merged by the split merge kernel.  A row that kept no
+    // key of this chunk leaves m = -inf, sums 0 and O 0.
+    const int64_t item =
+        ((static_cast<int64_t>(w.b) * a.sched.heads_q + w.h) * a.sched.n_heavy + (a.sched.n_qtiles - 1 - w.t)) *
+            a.sched.n_split + w.c;
+    const int row = wave * 32 + l32;
+    float* op = a.split_o + (item * kBlockQ + row) * D;
+#pragma unroll
+    for (int ob = 0; ob < C::kOBlocks; ++ob)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = ob * 32 + r4 * 8 + ln.hi * 4;
+        const f32x4 v4 = {st.o[ob][r4 * 4 + 0], st.o[ob][r4 * 4 + 1], st.o[ob][r4 * 4 + 2], st.o[ob][r4 * 4 + 3]};
+        *reinterpret_cast<f32x4*>(op + d0) = v4;
+      }
+    if (ln.hi == 0) {
+      float* sp = a.split_stats + item * 3 * kBlockQ + row;
+      sp[0] = st.m;
+      sp[kBlockQ] = l_tot;
+      sp[2 * kBlockQ] = b0 + b1;
+    }
+    return;
+  }
   if (ln.qrow < N) {
     const float inv = 1.0f / (b0 + b1);
     const int64_t orow =

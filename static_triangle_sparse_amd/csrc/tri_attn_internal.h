@@ -31,23 +31,35 @@ int validate_mask(const tri_mask_params* mp);
 //   * inside an XCD, blocks run position-major, then stream, then the G query
 //     heads of the group, so the blocks in flight on one XCD work on the same
 //     K/V window;
+//   * an XCD places its blocks on its 32 CUs in a fixed rotation, in order,
+//     waiting for the chosen CU to have room (measured on MI355X).  With G a
+//     divisor of 32, head slot j of every position would land on the same
+//     CUs, and heads of unequal cost (per-head windows) would leave most CUs
+//     idle behind the busiest ones; so the head given to slot j rotates by one
+//     per 32-block cycle of the XCD (the cycle of the position's first slot,
+//     keeping the heads of a position a permutation);
 //   * positions are ordered heaviest first: for the triangle mask the query
 //     tiles holding last-Q rows (which read every earlier key) come first in
 //     descending order, then the rest ascending; for the causal mask the
-//     tiles run in descending order.
-// Positions past the last tile of a stream leave the block idle (t = -1).
+//     tiles run in descending order;
+//   * with a split (n_split > 1, triangle only), each heavy tile becomes
+//     n_split chunk items, chunk c walking list entries [c C, (c + 1) C) of
+//     the tile's row (C = chunk_tiles); the chunk items come first.
+// Positions past the last item of a stream leave the block idle (t = -1).
 struct Schedule {
   int32_t batch, heads_q, heads_kv, group;  // group = heads_q / heads_kv
   int32_t n_qtiles;                          // query tiles of 128 rows
   int32_t causal;                            // 1: causal order, 0: triangle order
   int32_t n_heavy;                           // triangle: tiles with last-Q rows
+  int32_t n_split;                           // chunk items per heavy tile (1: no split)
   int32_t streams;                           // S: streams per KV group
   int32_t streams_per_xcd;                   // spx
-  int32_t positions;                         // P = ceil(n_qtiles / S)
+  int32_t positions;                         // P = ceil(items per group / S)
   int64_t grid;                              // 8 * spx * P * group
 };
 
 constexpr int kNumXcd = 8;
+constexpr int kCusPerXcd = 32;
 
 constexpr int32_t gcd_i32(int32_t a, int32_t b) {
   while (b) {
@@ -58,9 +70,10 @@ constexpr int32_t gcd_i32(int32_t a, int32_t b) {
   return a;
 }
 
-// block_q: rows per query tile; last_q: clamped to [0, N].
+// block_q: rows per query tile; last_q: clamped to [0, N]; n_split: chunk
+// items per heavy triangle tile (1: none).
 constexpr Schedule make_schedule(int32_t batch, int32_t heads_q, int32_t heads_kv, int64_t N,
-                                 int32_t block_q, bool causal, int64_t last_q) {
+                                 int32_t block_q, bool causal, int64_t last_q, int32_t n_split = 1) {
   Schedule s{};
   s.batch = batch;
   s.heads_q = heads_q;
@@ -74,16 +87,19 @@ constexpr Schedule make_schedule(int32_t batch, int32_t heads_q, int32_t heads_k
     const int64_t first_heavy = (N - last_q) / block_q;  // tile of row N - last_q
     s.n_heavy = static_cast<int32_t>(s.n_qtiles - first_heavy);
   }
+  s.n_split = (!causal && s.n_heavy > 0 && n_split > 1) ? n_split : 1;
   const int32_t n_groups = batch * heads_kv;
   s.streams = kNumXcd / gcd_i32(n_groups, kNumXcd);
   s.streams_per_xcd = n_groups * s.streams / kNumXcd;
-  s.positions = (s.n_qtiles + s.streams - 1) / s.streams;
+  const int64_t items = static_cast<int64_t>(s.n_heavy) * (s.n_split - 1) + s.n_qtiles;
+  s.positions = static_cast<int32_t>((items + s.streams - 1) / s.streams);
   s.grid = static_cast<int64_t>(kNumXcd) * s.streams_per_xcd * s.positions * s.group;
   return s;
 }
 
 struct WorkItem {
   int32_t b, h, t;  // t = -1: idle block
+  int32_t c;        // chunk of a split heavy tile, or -1 (the whole row)
 };
 
 constexpr WorkItem schedule_item(const Schedule& s, int64_t bid) {
@@ -93,19 +109,24 @@ constexpr WorkItem schedule_item(const Schedule& s, int64_t bid) {
   const int64_t pi = u / per_pos;
   const int64_t rem = u % per_pos;
   const int64_t si = rem / s.group;
-  const int32_t hh = static_cast<int32_t>(rem % s.group);
+  const int64_t cycle = (pi * per_pos + si * s.group) / kCusPerXcd;
+  const int32_t hh = static_cast<int32_t>((rem % s.group + cycle) % s.group);
   const int64_t stream = x * s.streams_per_xcd + si;
   const int32_t grp = static_cast<int32_t>(stream / s.streams);
   const int64_t p = pi * s.streams + stream % s.streams;
-  WorkItem w{-1, -1, -1};
-  if (bid < 0 || bid >= s.grid || p >= s.n_qtiles) return w;
+  WorkItem w{-1, -1, -1, -1};
+  const int64_t n_chunk_items = static_cast<int64_t>(s.n_heavy) * s.n_split;
+  if (bid < 0 || bid >= s.grid || p >= n_chunk_items - s.n_heavy + s.n_qtiles) return w;
   int32_t t = -1;
   if (s.causal) {
     t = s.n_qtiles - 1 - static_cast<int32_t>(p);
-  } else if (p < s.n_heavy) {
+  } else if (s.n_split > 1 && p < n_chunk_items) {
+    t = s.n_qtiles - 1 - static_cast<int32_t>(p / s.n_split);
+    w.c = static_cast<int32_t>(p % s.n_split);
+  } else if (s.n_split == 1 && p < s.n_heavy) {
     t = s.n_qtiles - 1 - static_cast<int32_t>(p);
   } else {
-    t = static_cast<int32_t>(p) - s.n_heavy;
+    t = static_cast<int32_t>(p - (s.n_split > 1 ? n_chunk_items : s.n_heavy));
   }
   w.b = grp / s.heads_kv;
   w.h = (grp % s.heads_kv) * s.group + hh;
@@ -146,11 +167,30 @@ struct AttnLaunch {
   const void* k8;
   const float* k8_scale;
   const int32_t* head_low_dist;
+  // split of heavy tiles (sched.n_split > 1): chunk items write unnormalised
+  // partials, item = ((b * heads_q + h) * n_heavy + (n_qtiles - 1 - t)) *
+  // n_split + c: O [item][128][d] f32 and (m, l, lb) [item][3][128] f32
+  int32_t chunk_tiles;
+  float* split_o;
+  float* split_stats;
   Schedule sched;
 };
 
 // Enqueue the gfx950 kernel; returns TRI_OK or TRI_ERR_HIP.
 int launch_attn_fwd(const AttnLaunch& a, void* stream);
+
+// Workspace of a split launch (byte offsets, each 256-aligned): per-row
+// statistics, then partial outputs.
+struct SplitWorkspace {
+  int64_t n_items;  // batch * heads_q * n_heavy * n_split
+  int64_t stats, o, total;
+};
+SplitWorkspace split_workspace(int64_t batch, int64_t heads_q, int64_t head_dim, int64_t n_heavy,
+                               int64_t n_split);
+
+// Enqueue the merge of the chunk partials into O and LSE (one thread per
+// (heavy tile row, 4 channels)); returns TRI_OK or TRI_ERR_HIP.
+int launch_split_merge(const AttnLaunch& a, void* stream);
 
 // ---------------------------------------------------------------- dynamic plan
 

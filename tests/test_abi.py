@@ -2,6 +2,7 @@
 header declares, validates every argument before touching HIP, and its block
 schedule covers each work item exactly once."""
 import ctypes
+import math
 import os
 import re
 
@@ -25,7 +26,8 @@ def test_header_symbols_are_exported():
     assert {"tri_attn_plan", "tri_attn_prefill", "dense_causal_prefill",
             "tri_attn_last_error", "tri_dyn_plan_sizes", "tri_dyn_plan",
             "tri_attn_prefill_lists", "tri_attn_plan_heads", "tri_attn_prefill_heads",
-            "tri_attn_quantize_k_sizes", "tri_attn_quantize_k", "tri_attn_prefill_tiered"} <= set(names)
+            "tri_attn_quantize_k_sizes", "tri_attn_quantize_k", "tri_attn_prefill_tiered",
+            "tri_attn_split_workspace_size", "tri_attn_prefill_split", "tri_attn_split_work_item"} <= set(names)
     lib = ctypes.CDLL(_abi.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -286,3 +288,115 @@ def test_schedule_puts_a_kv_group_on_one_xcd_and_heavy_tiles_first():
     seen, order = _cover(1, 32, 8, 8192, tsa.TRI_MASK_CAUSAL, 0)
     ts = [t for _, _, _, t in order]
     assert ts == sorted(ts, reverse=True)  # causal: heaviest (longest) tiles first
+
+
+# ----------------------------------------------------------------- split launch
+
+def _cover_split(B, Hq, Hkv, N, last_q, chunk):
+    _, _, _, _, grid = tsa.tri_attn_split_work_item(B, Hq, Hkv, N, last_q, chunk, 0)
+    nq = -(-N // 128)
+    nkt = -(-N // 64)
+    first_heavy = (N - min(last_q, N)) // 128 if last_q > 0 else nq
+    n_split = -(-nkt // chunk) if first_heavy < nq else 1
+    seen = {}
+    order = []
+    for bid in range(grid):
+        b, h, t, c = tsa.tri_attn_split_work_item(B, Hq, Hkv, N, last_q, chunk, bid)[:4]
+        if t < 0:
+            assert (b, h, c) == (-1, -1, -1)
+            continue
+        key = (b, h, t, c)
+        assert key not in seen, key
+        seen[key] = bid
+        order.append((bid, b, h, t, c))
+    want = set()
+    for b in range(B):
+        for h in range(Hq):
+            for t in range(nq):
+                if t >= first_heavy and n_split > 1:
+                    want |= {(b, h, t, c) for c in range(n_split)}
+                else:
+                    want.add((b, h, t, -1))
+    assert set(seen) == want
+    return seen, order, n_split
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,last_q,chunk", [
+    (1, 32, 8, 8192, 128, 16), (1, 32, 8, 131072, 128, 64), (2, 6, 3, 1000, 300, 3),
+    (1, 4, 1, 129, 1, 1), (3, 7, 7, 640, 0, 4), (1, 28, 4, 3000, 128, 8), (1, 2, 2, 64, 64, 2)])
+def test_split_schedule_covers_every_chunk_once(B, Hq, Hkv, N, last_q, chunk):
+    seen, order, n_split = _cover_split(B, Hq, Hkv, N, last_q, chunk)
+    if n_split > 1:
+        # the chunk items of the heavy tiles come first: no chunk item sits in a
+        # later row of positions (blocks 8 * streams_per_xcd * group apart)
+        # than a whole-row item
+        groups = B * Hkv
+        streams = 8 // math.gcd(groups, 8)
+        per_row = 8 * (groups * streams // 8) * (Hq // Hkv)
+        rows_c = [bid // per_row for bid, _, _, _, c in order if c >= 0]
+        rows_n = [bid // per_row for bid, _, _, _, c in order if c < 0]
+        assert not rows_n or max(rows_c) <= min(rows_n)
+
+
+def test_split_workspace_size_and_arguments():
+    lib = tsa.load()
+    t = _good_tensors(B=1, Hq=4, Hkv=2, N=1000, d=128)
+    mp = tsa.mask_params(1000, "triangle", 16, 128, 64)
+    n = ctypes.c_int64()
+    assert lib.tri_attn_split_workspace_size(ctypes.byref(t), ctypes.byref(mp), 4, ctypes.byref(n)) == tsa.TRI_OK
+    # one heavy tile (rows 936..999 sit in tile 7), ceil(16 / 4) = 4 chunks,
+    # per chunk 128 rows x (3 statistics + 128 channels) f32
+    items = 1 * 4 * 1 * 4
+    assert n.value == -(-items * 3 * 128 * 4 // 256) * 256 + -(-items * 128 * 128 * 4 // 256) * 256
+    assert tsa.tri_attn_split_workspace_size(t, mp, 4) == n.value
+    assert tsa.tri_attn_split_workspace_size(t, tsa.mask_params(1000, "triangle", 16, 128, 0), 4) == 0
+    for bad in (0, -3):
+        assert lib.tri_attn_split_workspace_size(ctypes.byref(t), ctypes.byref(mp), bad,
+                                                 ctypes.byref(n)) == tsa.TRI_ERR_INVALID
+    causal = tsa.mask_params(1000, "causal")
+    assert lib.tri_attn_split_workspace_size(ctypes.byref(t), ctypes.byref(causal), 4,
+                                             ctypes.byref(n)) == tsa.TRI_ERR_INVALID
+    # launch-side validation, all before any HIP call
+    dev = 1 << 24
+    need = tsa.tri_attn_split_workspace_size(t, mp, 4)
+    call = lambda mp_, hs, hw, ws, nbytes, chunk=4: lib.tri_attn_prefill_split(
+        ctypes.byref(t), ctypes.byref(mp_), hs, hw, dev, dev, dev, chunk, ws, nbytes, None)
+    assert call(mp, None, None, dev, need - 1) == tsa.TRI_ERR_CAPACITY
+    assert call(mp, None, None, None, need) == tsa.TRI_ERR_INVALID
+    assert call(mp, None, None, dev + 128, need) == tsa.TRI_ERR_INVALID          # not 256-aligned
+    assert call(mp, dev, None, dev, need) == tsa.TRI_ERR_INVALID                  # sink without window
+    assert call(mp, None, None, dev, need, chunk=0) == tsa.TRI_ERR_INVALID
+    assert call(causal, None, None, dev, need) == tsa.TRI_ERR_INVALID
+    assert lib.tri_attn_prefill_split(ctypes.byref(t), ctypes.byref(mp), None, None, None, dev, dev, 4,
+                                      dev, need, None) == tsa.TRI_ERR_INVALID
+    other = tsa.mask_params(999, "triangle", 16, 128, 64)
+    assert call(other, None, None, dev, need) == tsa.TRI_ERR_INVALID
+    z = _good_tensors(N=0)
+    mz = tsa.mask_params(0, "triangle", 16, 128, 64)
+    assert lib.tri_attn_prefill_split(ctypes.byref(z), ctypes.byref(mz), None, None, dev, dev, dev, 4,
+                                      None, 0, None) == tsa.TRI_OK
+
+
+def test_schedule_balances_unequal_heads_over_the_cu_rotation():
+    # An XCD places its blocks on its 32 CUs in a fixed rotation (block u of
+    # the XCD on CU slot u % 32).  With per-head windows cycling over the 4
+    # heads of a group, every CU slot must still receive every head, so the
+    # per-CU work stays within a few percent of the mean.
+    N, Hq, Hkv = 32768, 32, 8
+    mp = tsa.mask_params(N, "triangle", 0, 1, 128)
+    window = [512 << (h % 4) for h in range(Hq)]
+    rp, _, _ = tsa.tri_attn_plan_heads(mp, np.zeros(Hq, np.int64), np.asarray(window, np.int64))
+    nq = N // 128
+    lens = np.diff(rp.astype(np.int64)).reshape(Hq, nq)
+    grid = tsa.tri_attn_work_item(1, Hq, Hkv, N, tsa.TRI_MASK_TRIANGLE, 128, 0)[3]
+    work = np.zeros((8, 32))
+    heads = [[set() for _ in range(32)] for _ in range(8)]
+    for bid in range(grid):
+        b, h, t, _ = tsa.tri_attn_work_item(1, Hq, Hkv, N, tsa.TRI_MASK_TRIANGLE, 128, bid)
+        if t < 0 or t == nq - 1:      # the last-Q tiles are the same for every head
+            continue
+        x, u = bid % 8, bid // 8
+        work[x, u % 32] += lens[h, t]
+        heads[x][u % 32].add(h % 4)
+    assert all(len(s) == 4 for row in heads for s in row)
+    assert work.max() / work.mean() < 1.05
