@@ -264,9 +264,28 @@ def bench_per_head(t, args, cfg, d, Hq, B, dev, stream):
     flops = 4.0 * 128 * 64 * d * plan.k_tile.size * B  # the plan lists every head
     tf = flops / (ms * 1e-3) / 1e12
     print(f"[bench] per-head triangle: {ms:.3f} ms/layer, {tf:.0f} TFLOP/s", file=sys.stderr, flush=True)
-    return {"windows": "512,1024,2048,4096 cycling", "sinks": "0,128 cycling", "ms": round(ms, 4),
-            "kept_tiles": int(plan.k_tile.size), "tflops": round(tf, 2),
-            "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+    out = {"windows": "512,1024,2048,4096 cycling", "sinks": "0,128 cycling", "ms": round(ms, 4),
+           "kept_tiles": int(plan.k_tile.size), "tflops": round(tf, 2),
+           "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+    # the same layer with every head's window 512: bound by the last-Q lists
+    # unless they are split over workgroups (tri_attn_prefill_split)
+    short = tsa.device_plan(cfg["N"], "triangle", cfg["sink"], 512, cfg["last_q"], dev)
+    plain = lambda: tsa.tri_attn_prefill(t, short.mp, short.d_row_ptr.data_ptr(), short.d_k_tile.data_ptr(),
+                                         short.d_flags.data_ptr(), stream)
+    chunk = 128
+    ws = tsa.split_workspace(tsa.tri_attn_split_workspace_size(t, short.mp, chunk), dev)
+    split = lambda: tsa.tri_attn_prefill_split(t, short.mp, None, None, short.d_row_ptr.data_ptr(),
+                                               short.d_k_tile.data_ptr(), short.d_flags.data_ptr(), chunk,
+                                               ws.data_ptr(), ws.numel(), stream)
+    plain_ms, _ = time_launches(plain, args.steps, args.warmup)
+    split_ms, _ = time_launches(split, args.steps, args.warmup)
+    print(f"[bench] window 512: {plain_ms:.3f} ms, last-Q lists split in chunks of {chunk}: {split_ms:.3f} ms",
+          file=sys.stderr, flush=True)
+    out["window512"] = {"ms": round(plain_ms, 4), "split_ms": round(split_ms, 4), "chunk_tiles": chunk,
+                        "kept_tiles_per_head": int(short.k_tile.size),
+                        "split_pct_bf16_peak": round(100 * 4.0 * 128 * 64 * d * short.k_tile.size * Hq * B /
+                                                     (split_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    return out
 
 
 def bench_tiered(t, args, cfg, plan, tri_ms, d, Hq, B, dev, stream):
