@@ -112,3 +112,19 @@ def test_llama_128k_split_sampled(dev):
     idx = torch.from_numpy(rows).to(dev)
     err, rel = gu.check(o[:, :, idx], lse[:, :, idx], ro, rl, "128K split")
     gu.note(f"  max|dO|={err:.2e} max rel dLSE={rel:.2e}")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,last_q,chunk", [(2, 4, 2, 600, 64, 10 ** 6, 2), (3, 2, 1, 257, 128, 200, 1)])
+def test_split_batches_per_head_and_whole_rows(dev, B, Hq, Hkv, N, d, last_q, chunk):
+    # last_q >= N makes every query tile a last-Q tile (all rows split)
+    gu.note(f"split per-head B={B} N={N} d={d} last_q={last_q} chunk={chunk}")
+    sink, window = [0, 32, 64, 7][:Hq], [16, 100, 300, 64][:Hq]
+    bits, (q, k, v) = gu.make_inputs(311 + N, B, Hq, Hkv, N, d, dev)
+    hp = tsa.head_plan(N, sink, window, last_q, dev)
+    o, lse = run_split(q, k, v, chunk, torch.bfloat16, mode="triangle_heads", plan=hp)
+    qf, kf, vf = (gu.as_f64(x) for x in bits)
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        ro, rl = oatt.attention(qf[:, h:h + 1], kf[:, g:g + 1], vf[:, g:g + 1], "triangle",
+                                sink[h], window[h], last_q)
+        gu.check(o[:, h:h + 1], lse[:, h:h + 1], ro, rl, f"split B={B} h={h}")
