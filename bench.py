@@ -334,6 +334,8 @@ def main(argv=None):
                     help="precision tiers: fp8 scores on key tiles at least this many keys behind "
                          "the query tile (negative: disable the tiered layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the 2.5 s shader-clock run (profiling runs)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -378,7 +380,7 @@ def main(argv=None):
           f"{runs['cold']['median_ms']:.3f} ms", file=sys.stderr, flush=True)
     # the same launches for ~2.5 s more, with the shader clock read meanwhile:
     # the fraction of the MFMA peak at the clock the chip actually ran
-    sclk, detail = measure_clock(tri, tri_ms)
+    sclk, detail = (None, "skipped (--no-clock)") if args.no_clock else measure_clock(tri, tri_ms)
     at_clock = {"sclk_mhz": round(sclk, 1) if sclk else None, "how": detail}
     if sclk:
         peak_at = 256 * 4096 * sclk * 1e6 / 1e12
