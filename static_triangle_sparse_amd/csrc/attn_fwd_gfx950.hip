@@ -153,6 +153,17 @@ __device__ __forceinline__ void drop_keys(float (&s)[16], uint32_t drop, std::in
   ((s[R] = drop_if<(R >> 2) * 8 + (R & 3)>(s[R], drop, kNegInfBits)), ...);
 }
 
+// An MFMA result may be read by a VALU instruction only some wait states
+// after the MFMA issued (the matrix core writes it over its passes).  The
+// compiler inserts them before its own instructions, but not before inline
+// assembly, which it does not look into.  The score helpers below that read
+// MFMA results in assembly (masking, row max) therefore first pass the block
+// through this fence: 21 wait states, enough for the longest MFMA here (the
+// 16-pass fp8 32x32x64); the "+v" operand orders every later read after it.
+__device__ __forceinline__ void mfma_result_fence(f32x16& s) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(s));
+}
+
 __device__ __forceinline__ void wait_vmcnt0() {
   // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -310,6 +321,7 @@ struct Kernel {
       }
     }
     if (partial) {
+      mfma_result_fence(s);  // the masking below reads the MFMA result in assembly
       // bit o of `drop` is set when key base + o is masked for this lane's row
       const int base = key0 + kb * 32;
       const uint32_t keep = low_bits(ln.hi_lim - base + 1) &
@@ -326,7 +338,10 @@ struct Kernel {
   }
 
   // Row max over the 32 keys of a score block (16 here, 16 in lane ^ 32).
-  static __device__ __forceinline__ float row_max(const f32x16& s) {
+  // Reads the block in assembly: fenced first (the block may be fresh from
+  // the MFMA).
+  static __device__ __forceinline__ float row_max(f32x16& s) {
+    mfma_result_fence(s);
     const float a0 = vmax3(s[0], s[1], s[2]), a1 = vmax3(s[3], s[4], s[5]);
     const float a2 = vmax3(s[6], s[7], s[8]), a3 = vmax3(s[9], s[10], s[11]);
     const float a4 = vmax3(s[12], s[13], s[14]);
@@ -350,7 +365,7 @@ struct Kernel {
                                                       State& st, int kb, int key0, bool partial,
                                                       float c_log2, bool& need_ref, bool low = false,
                                                       float sc = 1.0f) {
-    const f32x16 s = scores(stage, ln, st, kb, key0, partial, low);
+    f32x16 s = scores(stage, ln, st, kb, key0, partial, low);
     const float c = low ? c_log2 * sc : c_log2;
     if (need_ref) {
       // a row with no kept key so far has O = 0 and l = 0: its reference may still move
@@ -414,7 +429,8 @@ struct Kernel {
   // Exact-max pass over one 32-key half: scores and row max only.
   static __device__ __forceinline__ void max_half(const char LDS_AS* stage, const Lane& ln, State& st, int kb,
                                                   int key0, bool partial, bool low = false, float sc = 1.0f) {
-    const float mx = row_max(scores(stage, ln, st, kb, key0, partial, low));
+    f32x16 s = scores(stage, ln, st, kb, key0, partial, low);
+    const float mx = row_max(s);
     st.mt = fmaxf(st.mt, low ? mx * sc : mx);
   }
 };

@@ -76,3 +76,32 @@ def test_llama_128k_per_head_windows_sampled(dev):
         ro, rl = oatt.attention(qf[:, h:h + 1], kf[:, g:g + 1], vf[:, g:g + 1], "triangle", sink[h],
                                 window[h], 128, rows=rows)
         gu.check(o[:, h:h + 1][:, :, idx], lse[:, h:h + 1][:, :, idx], ro, rl, f"128K head {h}")
+
+
+def test_per_head_skips_tiles_and_is_deterministic(dev):
+    # heads of one KV group with different windows: NaN in every key tile that
+    # no head of the group keeps for query tile 40 leaves that tile's rows of
+    # every head bit-identical; two runs agree bit for bit
+    gu.note("per-head: NaN poison of skipped tiles and determinism, N=8192")
+    N, Hq = 8192, 4
+    sink, window = [0, 128, 0, 128], [256, 512, 1024, 2048]
+    _, (q, k, v) = gu.make_inputs(47, 1, Hq, 1, N, 128, dev)
+    plan = tsa.head_plan(N, sink, window, 0, dev)
+    o_ref, l_ref = run_heads(q, k, v, plan, torch.bfloat16)
+    o_b, l_b = run_heads(q, k, v, plan, torch.bfloat16)
+    assert torch.equal(o_ref, o_b) and torch.equal(l_ref, l_b)
+    nq = N // 128
+    t = 40
+    kept = set()
+    for h in range(Hq):
+        r = h * nq + t
+        kept |= set(plan.k_tile[plan.row_ptr[r]:plan.row_ptr[r + 1]].tolist())
+    k2, v2 = k.clone(), v.clone()
+    for kt in range(N // 64):
+        if kt not in kept:
+            k2[:, :, kt * 64:(kt + 1) * 64] = float("nan")
+            v2[:, :, kt * 64:(kt + 1) * 64] = float("nan")
+    o2, l2 = run_heads(q, k2, v2, plan, torch.bfloat16)
+    rows = slice(t * 128, (t + 1) * 128)
+    assert torch.isfinite(o2[:, :, rows]).all()
+    assert torch.equal(o2[:, :, rows], o_ref[:, :, rows]) and torch.equal(l2[:, :, rows], l_ref[:, :, rows])

@@ -128,3 +128,25 @@ def test_split_batches_per_head_and_whole_rows(dev, B, Hq, Hkv, N, d, last_q, ch
         ro, rl = oatt.attention(qf[:, h:h + 1], kf[:, g:g + 1], vf[:, g:g + 1], "triangle",
                                 sink[h], window[h], last_q)
         gu.check(o[:, h:h + 1], lse[:, h:h + 1], ro, rl, f"split B={B} h={h}")
+
+
+def test_split_skips_tiles_and_is_deterministic(dev):
+    gu.note("split: NaN poison of skipped tiles and determinism, N=8192")
+    N, Hq = 8192, 4
+    kw = dict(mode="triangle", sink=128, window=1024, last_q=128)
+    _, (q, k, v) = gu.make_inputs(43, 1, Hq, 1, N, 128, dev)
+    o_ref, l_ref = run_split(q, k, v, 16, torch.bfloat16, **kw)
+    o_b, l_b = run_split(q, k, v, 16, torch.bfloat16, **kw)
+    assert torch.equal(o_ref, o_b) and torch.equal(l_ref, l_b)
+    plan = tsa.device_plan(N, "triangle", 128, 1024, 128, dev)
+    t = 30
+    kept = set(plan.k_tile[plan.row_ptr[t]:plan.row_ptr[t + 1]].tolist())
+    k2, v2 = k.clone(), v.clone()
+    for kt in range(N // 64):
+        if kt not in kept:
+            k2[:, :, kt * 64:(kt + 1) * 64] = float("nan")
+            v2[:, :, kt * 64:(kt + 1) * 64] = float("nan")
+    o2, l2 = run_split(q, k2, v2, 16, torch.bfloat16, **kw)
+    rows = slice(t * 128, (t + 1) * 128)
+    assert torch.isfinite(o2[:, :, rows]).all()
+    assert torch.equal(o2[:, :, rows], o_ref[:, :, rows]) and torch.equal(l2[:, :, rows], l_ref[:, :, rows])

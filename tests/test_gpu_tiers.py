@@ -122,3 +122,38 @@ def test_llama_128k_tiered_sampled(dev):
                                   kw["window"], kw["last_q"], [1024], rows=rows)
         idx = torch.from_numpy(rows).to(dev)
         gu.check(o[:, h:h + 1][:, :, idx], lse[:, h:h + 1][:, :, idx], ro, rl, f"128K head {h}")
+
+
+def test_tiered_skips_tiles_and_is_deterministic(dev):
+    # NaN in every key tile query tile 40 does not keep (K and V, so the fp8
+    # copy of those half-tiles holds NaN scales and codes) leaves that tile's
+    # rows bit-identical; two runs agree bit for bit
+    gu.note("tiered: NaN poison of skipped tiles and determinism, N=8192")
+    N, Hq = 8192, 4
+    kw = dict(sink=128, window=2048, last_q=0)
+    dist = [0, 512, 1024, 10 ** 6]
+    _, (q, k, v) = gu.make_inputs(41, 1, Hq, 1, N, 128, dev)
+
+    def run(k_, v_):
+        qk = tsa.quantize_k(q, k_)
+        o = torch.empty((1, Hq, N, 128), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((1, Hq, N), dtype=torch.float32, device=dev)
+        tsa.prefill(q, k_, v_, mode="tiered", plan=qk, low_dist=dist, o_dtype=torch.bfloat16, out=o,
+                    lse=lse, **kw)
+        torch.cuda.synchronize()
+        return o, lse
+    o_ref, l_ref = run(k, v)
+    o_b, l_b = run(k, v)
+    assert torch.equal(o_ref, o_b) and torch.equal(l_ref, l_b)
+    plan = tsa.device_plan(N, "triangle", device=dev, **kw)
+    t = 40
+    kept = set(plan.k_tile[plan.row_ptr[t]:plan.row_ptr[t + 1]].tolist())
+    k2, v2 = k.clone(), v.clone()
+    for kt in range(N // 64):
+        if kt not in kept:
+            k2[:, :, kt * 64:(kt + 1) * 64] = float("nan")
+            v2[:, :, kt * 64:(kt + 1) * 64] = float("nan")
+    o2, l2 = run(k2, v2)
+    rows = slice(t * 128, (t + 1) * 128)
+    assert torch.isfinite(o2[:, :, rows]).all()
+    assert torch.equal(o2[:, :, rows], o_ref[:, :, rows]) and torch.equal(l2[:, :, rows], l_ref[:, :, rows])
