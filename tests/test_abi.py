@@ -400,3 +400,50 @@ def test_schedule_balances_unequal_heads_over_the_cu_rotation():
         heads[x][u % 32].add(h % 4)
     assert all(len(s) == 4 for row in heads for s in row)
     assert work.max() / work.mean() < 1.05
+
+
+# ----------------------------------------------------------------- precision tiers
+
+def test_quantize_k_sizes_and_arguments():
+    lib = tsa.load()
+    t = _good_tensors(B=2, Hq=4, Hkv=2, N=1000, d=128)
+    nb, ns = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.tri_attn_quantize_k_sizes(ctypes.byref(t), ctypes.byref(nb), ctypes.byref(ns)) == tsa.TRI_OK
+    assert nb.value == 2 * 2 * 1000 * 128 and ns.value == 2 * 2 * 32   # ceil(1000 / 32) = 32
+    assert tsa.tri_attn_quantize_k_sizes(t) == (nb.value, ns.value)
+    assert lib.tri_attn_quantize_k_sizes(ctypes.byref(t), None, ctypes.byref(ns)) == tsa.TRI_ERR_INVALID
+    dev = 1 << 24
+    assert lib.tri_attn_quantize_k(ctypes.byref(t), None, dev, None) == tsa.TRI_ERR_INVALID
+    assert lib.tri_attn_quantize_k(ctypes.byref(t), dev + 8, dev, None) == tsa.TRI_ERR_INVALID  # 16-byte
+    assert lib.tri_attn_quantize_k(ctypes.byref(t), dev, dev + 2, None) == tsa.TRI_ERR_INVALID  # 4-byte
+    bad = _good_tensors(d=96)
+    assert lib.tri_attn_quantize_k(ctypes.byref(bad), dev, dev, None) == tsa.TRI_ERR_UNSUPPORTED
+    z = _good_tensors(N=0)
+    assert lib.tri_attn_quantize_k(ctypes.byref(z), dev, dev, None) == tsa.TRI_OK
+
+
+def test_prefill_tiered_rejects_bad_arguments():
+    lib = tsa.load()
+    t = _good_tensors(B=1, Hq=4, Hkv=2, N=1000, d=128)
+    mp = tsa.mask_params(1000, "triangle", 16, 128, 64)
+    dev = 1 << 24
+    good = [dev, dev, dev, dev, dev, dev]   # low_dist, k8, scale, row_ptr, k_tile, flags
+
+    def call(mp_, args):
+        return lib.tri_attn_prefill_tiered(ctypes.byref(t), ctypes.byref(mp_), *args, None)
+    for i in range(6):
+        args = list(good)
+        args[i] = None
+        assert call(mp, args) == tsa.TRI_ERR_INVALID, i
+    for i, off in ((0, 2), (1, 8), (2, 2), (3, 2), (4, 2)):   # int32 4-byte, fp8 K 16-byte
+        args = list(good)
+        args[i] = dev + off
+        assert call(mp, args) == tsa.TRI_ERR_INVALID, i
+    assert call(tsa.mask_params(1000, "causal"), good) == tsa.TRI_ERR_INVALID
+    assert call(tsa.mask_params(999, "triangle", 16, 128, 64), good) == tsa.TRI_ERR_INVALID
+    odd = tsa.mask_params(1000, "triangle", 16, 128, 64)
+    odd.block_k = 32
+    assert call(odd, good) == tsa.TRI_ERR_UNSUPPORTED
+    z = _good_tensors(N=0)
+    mz = tsa.mask_params(0, "triangle", 16, 128, 64)
+    assert lib.tri_attn_prefill_tiered(ctypes.byref(z), ctypes.byref(mz), *good, None) == tsa.TRI_OK
