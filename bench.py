@@ -11,7 +11,7 @@ Prints one JSON line.  ``value`` is kept-tile TFLOP/s: 4 * 128 * 64 * d FLOPs
 per kept (query tile, key tile) pair per query head (partial tiles count in
 full), divided by the measured time per layer.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--config 3]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 10] [--config 3]
 """
 from __future__ import annotations
 
@@ -322,7 +322,7 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3, choices=sorted(CONFIGS))
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--no-dense", action="store_true")
