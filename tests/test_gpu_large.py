@@ -39,3 +39,25 @@ def test_llama_layer_sampled_rows(dev, N):
         # every row written (no NaN left by an unwritten row)
         assert torch.isfinite(o).all() and torch.isfinite(lse).all()
         del o, lse
+
+
+@pytest.mark.parametrize("N,Hq,Hkv,seed", [(65536, 32, 8, 1012), (131072, 28, 4, 1020)])
+def test_stack_layer_shapes_sampled_rows(dev, N, Hq, Hkv, seed):
+    # the layer shapes the stack benchmarks run: the Llama-shaped layer at 64K
+    # and the Qwen2.5-7B-shaped layer (28 query heads, 4 KV heads: 7 per
+    # group) at 128K, triangle and dense, bf16 O as timed
+    gu.note(f"stack layer N={N} Hq={Hq} Hkv={Hkv}: generating inputs")
+    bits, (q, k, v) = gu.make_inputs(seed, 1, Hq, Hkv, N, 128, dev)
+    nq = N // 128
+    for mode in ("triangle", "causal"):
+        gu.note(f"stack layer N={N} Hq={Hq} mode={mode}: kernel")
+        o, lse = gu.run(q, k, v, mode, o_dtype=torch.bfloat16, **KW)
+        assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+        tiles = (0, 16, nq // 3, nq - 1) if mode == "triangle" else (0, 17, nq - 1)
+        rows = np.concatenate([np.arange(t * 128, (t + 1) * 128) for t in tiles])
+        gu.note(f"stack layer N={N} mode={mode}: oracle on {rows.size} rows")
+        ro, rl = gu.oracle(bits, mode, rows=rows, **KW)
+        idx = torch.from_numpy(rows).to(dev)
+        err, rel = gu.check(o[:, :, idx], lse[:, :, idx], ro, rl, f"N={N} Hq={Hq} {mode}")
+        gu.note(f"  max|dO|={err:.2e} max rel dLSE={rel:.2e}")
+        del o, lse
