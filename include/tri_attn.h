@@ -251,15 +251,34 @@ int tri_attn_prefill_heads(const tri_attn_tensors* t, const tri_mask_params* mp,
  * aligned) holds, for each (batch, KV head), N rows of head_dim bytes in the
  * kernel's operand order (byte 64s + 32h + j of a row is channel
  * 64s + 16(j/8) + 8h + j%8); d_scale [batch, heads_kv, ceil(N/32)] f32.
+ *
+ * The page's two lower tiers are 4-bit and 8-bit: a second per-head boundary
+ * selects fp4 (e2m1, on the same matrix cores at twice the fp8 rate) for
+ * the farthest tiles.  The farthest tier wins: a tile is fp4 when
+ * 128*t - (64*kt + 63) >= fp4_dist[h], else fp8 when >= low_dist[h], else
+ * bf16.  fp4 scores use s_q = amax |q row| / 6, s_k = amax / 6 of the 32-key
+ * half, codes e2m1(clamp(x * 6 / amax, -6, 6)) rounded to nearest, ties to
+ * the even code.
+ *
+ * tri_attn_quantize_k4_sizes / tri_attn_quantize_k4 -- the fp4 copy of t->k:
+ * d_k4 (16-byte aligned) holds, per (batch, KV head), N rows of head_dim / 2
+ * bytes; 16-byte block 2s + h of a row holds the 32 elements e of k-step s,
+ * lane half h (channel 64s + 16(e/8) + 8h + e%8, as in the fp8 copy) at
+ * nibble e of the block; d_scale [batch, heads_kv, ceil(N/32)] f32.
  * tri_attn_prefill_tiered -- tri_attn_prefill with the LOW tiles scored from
  * d_k8 / d_scale (the output of tri_attn_quantize_k for the same K) and the
- * device int32 boundaries d_head_low_dist [heads_q]; Q is quantized in the
- * kernel.  A boundary larger than N gives the plain triangle layer.
+ * device int32 boundaries d_head_low_dist [heads_q], and, when
+ * d_head_fp4_dist, d_k4 and d_scale4 are given (all three, or all NULL for
+ * no fp4 tier), the farthest tiles from the fp4 copy; Q is quantized in the
+ * kernel.  Boundaries larger than N give the plain triangle layer.
  */
 int tri_attn_quantize_k_sizes(const tri_attn_tensors* t, int64_t* k8_bytes, int64_t* n_scales);
 int tri_attn_quantize_k(const tri_attn_tensors* t, void* d_k8, float* d_scale, void* stream);
+int tri_attn_quantize_k4_sizes(const tri_attn_tensors* t, int64_t* k4_bytes, int64_t* n_scales);
+int tri_attn_quantize_k4(const tri_attn_tensors* t, void* d_k4, float* d_scale, void* stream);
 int tri_attn_prefill_tiered(const tri_attn_tensors* t, const tri_mask_params* mp,
                             const int32_t* d_head_low_dist, const void* d_k8, const float* d_scale,
+                            const int32_t* d_head_fp4_dist, const void* d_k4, const float* d_scale4,
                             const int32_t* d_row_ptr, const int32_t* d_k_tile,
                             const uint8_t* d_flags, void* stream);
 

@@ -27,7 +27,7 @@ from ._abi import (  # noqa: F401
     tri_attn_prefill_heads, tri_attn_prefill_lists, tri_attn_prefill_tiered,
     tri_attn_quantize_k, tri_attn_quantize_k_sizes, tri_attn_work_item, tri_dyn_plan,
     tri_dyn_plan_sizes, tri_attn_prefill_split, tri_attn_split_work_item,
-    tri_attn_split_workspace_size,
+    tri_attn_split_workspace_size, tri_attn_quantize_k4, tri_attn_quantize_k4_sizes,
 )
 
 __all__ = [
@@ -152,24 +152,33 @@ def head_plan(seqlen, sink, window, last_q=0, device="cuda") -> HeadPlan:
 
 
 class QuantizedK:
-    """fp8 copy of K for the precision tiers (device uint8 k8, f32 scales)."""
+    """fp8 copy of K for the precision tiers (device uint8 k8, f32 scales),
+    and with fp4=True also the fp4 copy (k4, scale4)."""
 
-    def __init__(self, t: AttnTensors, device):
+    def __init__(self, t: AttnTensors, device, fp4: bool = False):
         import torch
         nbytes, nscales = tri_attn_quantize_k_sizes(t)
         self.k8 = torch.empty(max(16, nbytes), dtype=torch.uint8, device=device)
         self.scale = torch.empty(max(1, nscales), dtype=torch.float32, device=device)
+        self.k4 = self.scale4 = None
+        if fp4:
+            nbytes4, nscales4 = tri_attn_quantize_k4_sizes(t)
+            self.k4 = torch.empty(max(16, nbytes4), dtype=torch.uint8, device=device)
+            self.scale4 = torch.empty(max(1, nscales4), dtype=torch.float32, device=device)
 
     def run(self, t: AttnTensors, stream: int) -> None:
         tri_attn_quantize_k(t, self.k8.data_ptr(), self.scale.data_ptr(), stream)
+        if self.k4 is not None:
+            tri_attn_quantize_k4(t, self.k4.data_ptr(), self.scale4.data_ptr(), stream)
 
 
-def quantize_k(q, k, stream=None) -> QuantizedK:
-    """fp8 (e4m3) copy of k in the tiered kernel's layout, with its scales."""
+def quantize_k(q, k, stream=None, fp4=False) -> QuantizedK:
+    """fp8 (e4m3) copy of k in the tiered kernel's layout, with its scales
+    (and the fp4 (e2m1) copy with fp4=True)."""
     import torch
     o = torch.empty((1, 1, 1, 8), dtype=torch.bfloat16, device=k.device)  # not written
     t = make_tensors(q, k, k, o, None)
-    qk = QuantizedK(t, k.device)
+    qk = QuantizedK(t, k.device, fp4)
     s = (stream if stream is not None else torch.cuda.current_stream(k.device)).cuda_stream
     qk.run(t, s)
     return qk
@@ -207,7 +216,7 @@ def dyn_plan(q, k, alpha, scale=None, stream=None) -> DynPlan:
 
 
 def prefill(q, k, v, mode="triangle", sink=0, window=1, last_q=0, o_dtype=None, scale=None,
-            out=None, lse=None, stream=None, plan=None, low_dist=None, split=None):
+            out=None, lse=None, stream=None, plan=None, low_dist=None, split=None, fp4_dist=None):
     """One attention layer on the GPU; returns (o, lse).  ``mode`` is
     "triangle" (planned tile list), "triangle_heads" (a HeadPlan), "tiered"
     (fp8 far tiles), "causal" (dense layer) or "lists" (per-head tile lists
@@ -259,12 +268,19 @@ def prefill(q, k, v, mode="triangle", sink=0, window=1, last_q=0, o_dtype=None, 
         p = device_plan(N, "triangle", sink, window, last_q, q.device)
         # the device copy of the boundaries lives on the QuantizedK object, so it
         # outlives the enqueued kernel
-        plan.low_dist = torch.as_tensor(
-            np.minimum(np.asarray(low_dist, np.int64), np.iinfo(np.int32).max),
+        clip = lambda x: torch.as_tensor(
+            np.clip(np.asarray(x, np.int64), np.iinfo(np.int32).min, np.iinfo(np.int32).max),
             dtype=torch.int32).to(q.device)
+        plan.low_dist = clip(low_dist)
+        fp4_args = (None, None, None)
+        if fp4_dist is not None:
+            if plan.k4 is None:
+                raise ValueError("fp4_dist= needs a QuantizedK made with fp4=True")
+            plan.fp4_dist = clip(fp4_dist)
+            fp4_args = (plan.fp4_dist.data_ptr(), plan.k4.data_ptr(), plan.scale4.data_ptr())
         tri_attn_prefill_tiered(t, p.mp, plan.low_dist.data_ptr(), plan.k8.data_ptr(),
-                                plan.scale.data_ptr(), p.d_row_ptr.data_ptr(), p.d_k_tile.data_ptr(),
-                                p.d_flags.data_ptr(), s)
+                                plan.scale.data_ptr(), *fp4_args, p.d_row_ptr.data_ptr(),
+                                p.d_k_tile.data_ptr(), p.d_flags.data_ptr(), s)
     elif mode == "lists":
         if plan is None:
             raise ValueError("mode 'lists' needs plan= (a DynPlan)")

@@ -142,7 +142,13 @@ def load() -> ctypes.CDLL:
     lib.tri_attn_quantize_k.restype = ctypes.c_int
     lib.tri_attn_prefill_tiered.argtypes = [P(AttnTensors), P(MaskParams), ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.tri_attn_quantize_k4_sizes.argtypes = [P(AttnTensors), P(ctypes.c_int64), P(ctypes.c_int64)]
+    lib.tri_attn_quantize_k4_sizes.restype = ctypes.c_int
+    lib.tri_attn_quantize_k4.argtypes = [P(AttnTensors), ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+    lib.tri_attn_quantize_k4.restype = ctypes.c_int
     lib.tri_attn_prefill_tiered.restype = ctypes.c_int
     lib.tri_attn_split_workspace_size.argtypes = [P(AttnTensors), P(MaskParams), ctypes.c_int32,
                                                   P(ctypes.c_int64)]
@@ -298,11 +304,26 @@ def tri_attn_quantize_k(t: AttnTensors, d_k8: int, d_scale: int, stream: int) ->
 
 
 def tri_attn_prefill_tiered(t: AttnTensors, mp: MaskParams, d_low_dist: int, d_k8: int,
-                            d_scale: int, d_row_ptr: int, d_k_tile: int, d_flags: int,
-                            stream: int) -> None:
-    """Enqueue a triangle layer with fp8 scores on far tiles (device pointers)."""
+                            d_scale: int, d_fp4_dist, d_k4, d_scale4, d_row_ptr: int, d_k_tile: int,
+                            d_flags: int, stream: int) -> None:
+    """Enqueue a triangle layer with fp8 (and fp4: the three fp4 pointers, or
+    None for none) scores on far tiles (device pointers)."""
     _check(load().tri_attn_prefill_tiered(ctypes.byref(t), ctypes.byref(mp), d_low_dist, d_k8,
-                                          d_scale, d_row_ptr, d_k_tile, d_flags, stream))
+                                          d_scale, d_fp4_dist, d_k4, d_scale4, d_row_ptr, d_k_tile,
+                                          d_flags, stream))
+
+
+def tri_attn_quantize_k4_sizes(t: AttnTensors):
+    """(bytes of the fp4 K, number of f32 scales) for layer ``t``."""
+    nb = ctypes.c_int64()
+    ns = ctypes.c_int64()
+    _check(load().tri_attn_quantize_k4_sizes(ctypes.byref(t), ctypes.byref(nb), ctypes.byref(ns)))
+    return nb.value, ns.value
+
+
+def tri_attn_quantize_k4(t: AttnTensors, d_k4: int, d_scale: int, stream: int) -> None:
+    """Enqueue the fp4 copy of t.k (device pointers)."""
+    _check(load().tri_attn_quantize_k4(ctypes.byref(t), d_k4, d_scale, stream))
 
 
 def tri_attn_split_workspace_size(t: AttnTensors, mp: MaskParams, chunk_tiles: int) -> int:

@@ -163,7 +163,7 @@ using namespace triattn;
 
 extern "C" const char* tri_attn_last_error(void) { return g_error; }
 
-extern "C" int tri_attn_abi_version(void) { return 2; }
+extern "C" int tri_attn_abi_version(void) { return 3; }
 
 extern "C" int tri_attn_prefill(const tri_attn_tensors* t, const tri_mask_params* mp,
                                 const int32_t* d_row_ptr, const int32_t* d_k_tile,
@@ -471,32 +471,53 @@ extern "C" int tri_attn_quantize_k_sizes(const tri_attn_tensors* t, int64_t* k8_
   return TRI_OK;
 }
 
-extern "C" int tri_attn_quantize_k(const tri_attn_tensors* t, void* d_k8, float* d_scale,
-                                   void* stream) {
+namespace {
+int quantize_k(const tri_attn_tensors* t, void* d_out, float* d_scale, void* stream, bool fp4) {
   clear_error();
   int st = validate_tensors(t);
   if (st != TRI_OK) return st;
-  if (!d_k8 || !d_scale) return fail(TRI_ERR_INVALID, "d_k8 and d_scale must be non-NULL");
-  if (!aligned(d_k8, 16) || !aligned(d_scale, 4))
-    return fail(TRI_ERR_INVALID, "d_k8 must be 16-byte and d_scale 4-byte aligned");
+  if (!d_out || !d_scale) return fail(TRI_ERR_INVALID, "the K copy and d_scale must be non-NULL");
+  if (!aligned(d_out, 16) || !aligned(d_scale, 4))
+    return fail(TRI_ERR_INVALID, "the K copy must be 16-byte and d_scale 4-byte aligned");
   if (t->seqlen == 0) return TRI_OK;
   QuantLaunch a{};
+  a.fp4 = fp4 ? 1 : 0;
   a.k = t->k;
   memcpy(a.k_stride, t->k_stride, sizeof(a.k_stride));
   a.heads_kv = t->heads_kv;
   a.head_dim = t->head_dim;
   a.seqlen = static_cast<int32_t>(t->seqlen);
   a.n_blocks = static_cast<int64_t>(t->batch) * t->heads_kv * ((t->seqlen + 31) / 32);
-  a.k8 = d_k8;
+  a.k8 = d_out;
   a.scale = d_scale;
   return launch_quantize_k(a, stream);
+}
+}  // namespace
+
+extern "C" int tri_attn_quantize_k(const tri_attn_tensors* t, void* d_k8, float* d_scale, void* stream) {
+  return quantize_k(t, d_k8, d_scale, stream, false);
+}
+
+extern "C" int tri_attn_quantize_k4_sizes(const tri_attn_tensors* t, int64_t* k4_bytes, int64_t* n_scales) {
+  clear_error();
+  int st = validate_tensors(t);
+  if (st != TRI_OK) return st;
+  if (!k4_bytes || !n_scales) return fail(TRI_ERR_INVALID, "output pointers must be non-NULL");
+  *k4_bytes = static_cast<int64_t>(t->batch) * t->heads_kv * t->seqlen * (t->head_dim / 2);
+  *n_scales = static_cast<int64_t>(t->batch) * t->heads_kv * ((t->seqlen + 31) / 32);
+  return TRI_OK;
+}
+
+extern "C" int tri_attn_quantize_k4(const tri_attn_tensors* t, void* d_k4, float* d_scale, void* stream) {
+  return quantize_k(t, d_k4, d_scale, stream, true);
 }
 
 extern "C" int tri_attn_prefill_tiered(const tri_attn_tensors* t, const tri_mask_params* mp,
                                        const int32_t* d_head_low_dist, const void* d_k8,
-                                       const float* d_scale, const int32_t* d_row_ptr,
-                                       const int32_t* d_k_tile, const uint8_t* d_flags,
-                                       void* stream) {
+                                       const float* d_scale, const int32_t* d_head_fp4_dist,
+                                       const void* d_k4, const float* d_scale4,
+                                       const int32_t* d_row_ptr, const int32_t* d_k_tile,
+                                       const uint8_t* d_flags, void* stream) {
   clear_error();
   int st = validate_mask(mp);
   if (st != TRI_OK) return st;
@@ -514,6 +535,11 @@ extern "C" int tri_attn_prefill_tiered(const tri_attn_tensors* t, const tri_mask
   if (!aligned(d_head_low_dist, 4) || !aligned(d_k8, 16) || !aligned(d_scale, 4) ||
       !aligned(d_row_ptr, 4) || !aligned(d_k_tile, 4))
     return fail(TRI_ERR_INVALID, "misaligned array (fp8 K: 16 bytes, int32/float: 4 bytes)");
+  const int fp4_given = (d_head_fp4_dist != nullptr) + (d_k4 != nullptr) + (d_scale4 != nullptr);
+  if (fp4_given != 0 && fp4_given != 3)
+    return fail(TRI_ERR_INVALID, "the fp4 boundary, fp4 K and its scales go together (all NULL: no fp4 tier)");
+  if (fp4_given && (!aligned(d_head_fp4_dist, 4) || !aligned(d_k4, 16) || !aligned(d_scale4, 4)))
+    return fail(TRI_ERR_INVALID, "misaligned fp4 array (fp4 K: 16 bytes, int32/float: 4 bytes)");
   if (t->seqlen * t->head_dim >= (int64_t(1) << 31))
     return fail(TRI_ERR_UNSUPPORTED, "seqlen x head_dim must be < 2^31 bytes of fp8 K per head");
   if (t->seqlen == 0) return TRI_OK;
@@ -524,5 +550,8 @@ extern "C" int tri_attn_prefill_tiered(const tri_attn_tensors* t, const tri_mask
   a.k8 = d_k8;
   a.k8_scale = d_scale;
   a.head_low_dist = d_head_low_dist;
+  a.k4 = d_k4;
+  a.k4_scale = d_scale4;
+  a.head_fp4_dist = d_head_fp4_dist;
   return launch_attn_fwd(a, stream);
 }

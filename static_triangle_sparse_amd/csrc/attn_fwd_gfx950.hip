@@ -31,6 +31,7 @@
 // Output O = acc / sum(bf16 P) (stored bf16 round-to-nearest-even or f32) and
 // the natural-log LSE = scale * m + ln sum(P) are written once per row.
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
 
 #include <utility>
@@ -86,6 +87,10 @@ struct Cfg {
   static constexpr int kK8Stride = D + 16;
   static constexpr int kK8Blocks = (kHalf * kK8Stride + 1023) / 1024;
   static constexpr int kK8BlocksPerWave = (kK8Blocks + kWaves - 1) / kWaves;
+  // fp4 K of a far half: 32 rows of D / 2 bytes, padded by 16 bytes
+  static constexpr int kK4Stride = D / 2 + 16;
+  static constexpr int kK4Blocks = (kHalf * kK4Stride + 1023) / 1024;
+  static constexpr int kK4BlocksPerWave = (kK4Blocks + kWaves - 1) / kWaves;
   static constexpr int kQ8Steps = D / 64;  // k-steps of the fp8 S^T
   static constexpr int kQSteps = D / 16;   // k-steps of S^T = K Q^T
   static constexpr int kOBlocks = D / 32;  // 32-channel blocks of O^T
@@ -204,22 +209,33 @@ __device__ __forceinline__ void dma_source(int x, int stride, int& row, int& chu
 }
 
 // Quantized Q of the tiered kernel (empty otherwise).
-template <int D, bool kTiers>
+// kTiers: 0 none, 1 fp8 + bf16, 2 fp4 + fp8 + bf16
+template <int D, int kTiers>
 struct TierState {};
 template <int D>
-struct TierState<D, true> {
+struct TierState<D, 1> {
   i32x8 q8[Cfg<D>::kQ8Steps];  // fp8 e4m3 Q in the fp8 operand order
   float s_q;                   // its scale: row amax / 448
 };
-template <int D, bool kTiers>
+template <int D>
+struct TierState<D, 2> : TierState<D, 1> {
+  u32x4 q4[Cfg<D>::kQ8Steps];  // fp4 e2m1 Q in the fp4 operand order
+  float s_q4;                  // its scale: row amax / 6
+};
+template <int D, int kTiers>
 struct TierLane {};
 template <int D>
-struct TierLane<D, true> {
+struct TierLane<D, 1> {
   uint32_t k8_dma[Cfg<D>::kK8BlocksPerWave];
   int k8_rd;
 };
+template <int D>
+struct TierLane<D, 2> : TierLane<D, 1> {
+  uint32_t k4_dma[Cfg<D>::kK4BlocksPerWave];
+  int k4_rd;
+};
 
-template <int D, bool kOutBf16, bool kCausal, bool kTiers>
+template <int D, bool kOutBf16, bool kCausal, int kTiers>
 struct Kernel {
   using C = Cfg<D>;
 
@@ -283,6 +299,25 @@ struct Kernel {
     }
   }
 
+  // fp4 K of a far half (blocks of the K region) plus V, as issue_dma.
+  static __device__ __forceinline__ void issue_dma_fp4(char LDS_AS* stage, const Lane& ln, int wave,
+                                                       const u32x4& k4_rsrc, const u32x4& v_rsrc) {
+    if constexpr (kTiers >= 2) {
+#pragma unroll
+      for (int i = 0; i < C::kK4BlocksPerWave; ++i) {
+        const int blk = i * kWaves + wave;
+        if (C::kK4Blocks % kWaves == 0 || blk < C::kK4Blocks)
+          lds_dma16(k4_rsrc, ln.k4_dma[i], stage + blk * 1024);
+      }
+#pragma unroll
+      for (int i = 0; i < C::kVBlocksPerWave; ++i) {
+        const int blk = i * kWaves + wave;
+        if (C::kVBlocks % kWaves == 0 || blk < C::kVBlocks)
+          lds_dma16(v_rsrc, ln.v_dma[i], stage + C::kKBytes + blk * 1024);
+      }
+    }
+  }
+
   // S^T block of one 32-key half (kb): lane = query, 16 of the 32 keys per
   // lane; register r holds key key0 + 32 kb + 8 (r >> 2) + 4 hi + (r & 3).
   // Keys a PARTIAL tile drops are set to -inf.
@@ -290,14 +325,32 @@ struct Kernel {
   // v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales); its scores are left
   // in fp8 code units, s_q s_k times smaller than raw scores (the caller folds
   // that factor into its exponent and maxima).
+  // A far half (fp4) is scored the same way from fp4 K and Q (format code 4
+  // on both operands, 16 bytes per lane per 64-wide k-step).
   static __device__ __forceinline__ f32x16 scores(const char LDS_AS* stage, const Lane& ln, const State& st,
-                                                  int kb, int key0, bool partial, bool low = false) {
+                                                  int kb, int key0, bool partial, bool low = false,
+                                                  bool fp4 = false) {
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.0f;
     bool done = false;
-    if constexpr (kTiers) {
-      if (low) {
+    if constexpr (kTiers >= 2) {
+      if (fp4) {
+        const char LDS_AS* kp4 = stage + ln.k4_rd;
+#pragma unroll
+        for (int q = 0; q < C::kQ8Steps; ++q) {
+          const u32x4 a0 = *reinterpret_cast<const LDS_AS u32x4*>(kp4 + q * 32);
+          const i32x8 ka = {static_cast<int>(a0[0]), static_cast<int>(a0[1]), static_cast<int>(a0[2]),
+                            static_cast<int>(a0[3]), 0, 0, 0, 0};
+          const i32x8 qb = {static_cast<int>(st.q4[q][0]), static_cast<int>(st.q4[q][1]),
+                            static_cast<int>(st.q4[q][2]), static_cast<int>(st.q4[q][3]), 0, 0, 0, 0};
+          s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qb, s, 4, 4, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
+        }
+        done = true;
+      }
+    }
+    if constexpr (kTiers >= 1) {
+      if (low && !done) {
         const char LDS_AS* kp8 = stage + ln.k8_rd;
 #pragma unroll
         for (int q = 0; q < C::kQ8Steps; ++q) {
@@ -364,8 +417,8 @@ struct Kernel {
   static __device__ __forceinline__ void compute_half(const char LDS_AS* stage, const Lane& ln,
                                                       State& st, int kb, int key0, bool partial,
                                                       float c_log2, bool& need_ref, bool low = false,
-                                                      float sc = 1.0f) {
-    f32x16 s = scores(stage, ln, st, kb, key0, partial, low);
+                                                      float sc = 1.0f, bool fp4 = false) {
+    f32x16 s = scores(stage, ln, st, kb, key0, partial, low, fp4);
     const float c = low ? c_log2 * sc : c_log2;
     if (need_ref) {
       // a row with no kept key so far has O = 0 and l = 0: its reference may still move
@@ -428,14 +481,15 @@ struct Kernel {
 
   // Exact-max pass over one 32-key half: scores and row max only.
   static __device__ __forceinline__ void max_half(const char LDS_AS* stage, const Lane& ln, State& st, int kb,
-                                                  int key0, bool partial, bool low = false, float sc = 1.0f) {
-    f32x16 s = scores(stage, ln, st, kb, key0, partial, low);
+                                                  int key0, bool partial, bool low = false, float sc = 1.0f,
+                                                  bool fp4 = false) {
+    f32x16 s = scores(stage, ln, st, kb, key0, partial, low, fp4);
     const float mx = row_max(s);
     st.mt = fmaxf(st.mt, low ? mx * sc : mx);
   }
 };
 
-template <int D, bool kOutBf16, bool kCausal, bool kTiers>
+template <int D, bool kOutBf16, bool kCausal, int kTiers>
 __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch a) {
   using K = Kernel<D, kOutBf16, kCausal, kTiers>;
   using C = Cfg<D>;
@@ -507,7 +561,30 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
       ln.k8_dma[i] = static_cast<uint32_t>(min(row, kHalf - 1) * D + chunk * 16);
     }
   }
-  auto is_low = [&](int kt) -> bool { return kTiers && q0 - (kt * kBlockK + kBlockK - 1) >= low_dist; };
+  // fp4 tier (optional): rows of D / 2 bytes; a tile is fp4 when
+  // q0 - (64 kt + 63) >= this head's fp4 boundary (the farthest tier wins)
+  const char* k4base = nullptr;
+  const float* k4scale = nullptr;
+  int fp4_dist = INT_MAX;
+  if constexpr (kTiers >= 2) {
+    {
+      const int64_t bg = static_cast<int64_t>(w.b) * a.sched.heads_kv + g;
+      k4base = static_cast<const char*>(a.k4) + bg * N * (D / 2);
+      k4scale = a.k4_scale + bg * ((N + kHalf - 1) / kHalf);
+      fp4_dist = a.head_fp4_dist[w.h];
+    }
+    ln.k4_rd = l32 * C::kK4Stride + ln.hi * 16;
+#pragma unroll
+    for (int i = 0; i < C::kK4BlocksPerWave; ++i) {
+      const int x = (i * kWaves + wave) * 1024 + lane * 16;
+      const int row = x / C::kK4Stride;
+      int chunk = (x - row * C::kK4Stride) / 16;
+      if (chunk >= D / 32) chunk = 0;  // row padding: re-read chunk 0 (never used)
+      ln.k4_dma[i] = static_cast<uint32_t>(min(row, kHalf - 1) * (D / 2) + chunk * 16);
+    }
+  }
+  auto is_low = [&](int kt) __attribute__((always_inline)) -> bool { return kTiers && q0 - (kt * kBlockK + kBlockK - 1) >= low_dist; };
+  auto is_fp4 = [&](int kt) __attribute__((always_inline)) -> bool { return kTiers >= 2 && q0 - (kt * kBlockK + kBlockK - 1) >= fp4_dist; };
 
   // mask bounds of this lane's row: j <= hi_lim and (j < sink_lim or j >= win_lo);
   // per-head boundaries, when given, replace the layer's sink and window
@@ -545,7 +622,7 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
   // tile list in registers, 64 entries per batch (lane i holds entry e0 + i)
   int list_e0 = e_begin;
   int list_kt = 0, list_fl = 0;
-  auto load_list = [&](int e0) {
+  auto load_list = [&](int e0) __attribute__((always_inline)) {
     list_e0 = e0;
     if (!kCausal) {
       const int e = e0 + lane;
@@ -553,10 +630,10 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
       list_fl = e < e_end ? a.flags[e] : 0;
     }
   };
-  auto tile_of = [&](int e) -> int {
+  auto tile_of = [&](int e) __attribute__((always_inline)) -> int {
     return kCausal ? e : __builtin_amdgcn_readlane(list_kt, e - list_e0);
   };
-  auto partial_of = [&](int e, int kt) -> bool {
+  auto partial_of = [&](int e, int kt) __attribute__((always_inline)) -> bool {
     if (kCausal) {
       const int c1 = kt * kBlockK + kBlockK - 1;
       return c1 > q0 || c1 >= N;
@@ -565,7 +642,7 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
   };
 
   typename K::State st;
-  auto load_q = [&]() {
+  auto load_q = [&]() __attribute__((always_inline)) {
     const int qr = ln.qrow;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + w.b * a.q_stride[0] + w.h * a.q_stride[1] +
                          static_cast<int64_t>(qr) * a.q_stride[2] + ln.hi * 8;
@@ -580,16 +657,44 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
   // order: step q8 takes the bf16 k-steps 4 q8 .. 4 q8 + 3 of this lane
   // (channels 16 s + 8 hi + 0..7), so the fp8 K rows are stored with the same
   // channel order; scale = amax / 448.
-  auto make_q8 = [&]() {
-    if constexpr (kTiers) {
-      float amax = 0.0f;
+  // row amax of the bf16 Q just loaded (its two lane halves)
+  auto q_amax = [&]() __attribute__((always_inline)) -> float {
+    float amax = 0.0f;
 #pragma unroll
-      for (int q = 0; q < C::kQSteps; ++q)
+    for (int q = 0; q < C::kQSteps; ++q)
 #pragma unroll
-        for (int x = 0; x < 8; ++x) amax = fmaxf(amax, fabsf(static_cast<float>(st.q[q][x])));
-      float p0, p1;
-      pair_halves(amax, p0, p1);
-      amax = fmaxf(p0, p1);
+      for (int x = 0; x < 8; ++x) amax = fmaxf(amax, fabsf(static_cast<float>(st.q[q][x])));
+    float p0, p1;
+    pair_halves(amax, p0, p1);
+    return fmaxf(p0, p1);
+  };
+  // fp4 Q (three-tier kernel): word s of step q holds the 8 channels of bf16
+  // k-step 4 q + s, the element order of the fp4 K rows; scale = amax / 6
+  auto make_q4 = [&]() __attribute__((always_inline)) {
+    if constexpr (kTiers >= 2) {
+      const float amax = q_amax();
+      const float inv4 = amax > 0.0f ? 6.0f / amax : 0.0f;
+      st.s_q4 = amax / 6.0f;
+#pragma unroll
+      for (int q4 = 0; q4 < C::kQ8Steps; ++q4)
+#pragma unroll
+        for (int qs = 0; qs < 4; ++qs) {
+          float v[8];
+#pragma unroll
+          for (int x = 0; x < 8; ++x)
+            v[x] = fminf(fmaxf(static_cast<float>(st.q[4 * q4 + qs][x]) * inv4, -6.0f), 6.0f);
+          unsigned word = 0;
+          word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[0], v[1], 1.0f, 0);
+          word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[2], v[3], 1.0f, 1);
+          word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[4], v[5], 1.0f, 2);
+          word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[6], v[7], 1.0f, 3);
+          st.q4[q4][qs] = word;
+        }
+    }
+  };
+  auto make_q8 = [&]() __attribute__((always_inline)) {
+    if constexpr (kTiers >= 1) {
+      const float amax = q_amax();
       const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
       st.s_q = amax / 448.0f;
 #pragma unroll
@@ -608,8 +713,16 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
           }
     }
   };
-  load_q();
-  make_q8();
+  // the Q form of the first phase: fp4 Q in the three-tier kernel (fp8 Q is
+  // made at the fp4 -> fp8 boundary), else fp8 Q
+  auto first_q = [&]() __attribute__((always_inline)) {
+    load_q();
+    if constexpr (kTiers >= 2)
+      make_q4();
+    else
+      make_q8();
+  };
+  first_q();
   st.m = -INFINITY;
   st.neg_mc = 0.0f;
   st.mt = -INFINITY;
@@ -617,13 +730,18 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
 
   const float c_log2 = a.scale * kLog2e;
 
-  // copies of half kb of tile kt into a stage: bf16 K (high) or fp8 K (LOW), and V
-  auto dma = [&](char LDS_AS* stage, int kt, int kb, bool low) {
+  // copies of half kb of tile kt into a stage: bf16 K (tier 0), fp8 K (tier
+  // 1) or fp4 K (tier 2), and V
+  auto dma = [&](char LDS_AS* stage, int kt, int kb, int tier) __attribute__((always_inline)) {
     const int key0 = kt * kBlockK + kb * kHalf;
     // keys past the sequence end (the second half of a last tile can start
     // there) are outside the descriptor and land as zeros
     const int rows = max(N - key0, 0);
-    if (kTiers && low)
+    if (kTiers && tier == 2)
+      K::issue_dma_fp4(stage, ln, wave, buffer_rsrc(k4base + static_cast<int64_t>(key0) * (D / 2),
+                                                    static_cast<uint32_t>(rows * (D / 2))),
+                       buffer_rsrc(vbase + key0 * vs_b, static_cast<uint32_t>(rows * vs_b)));
+    else if (kTiers && tier == 1)
       K::issue_dma_low(stage, ln, wave, buffer_rsrc(k8base + static_cast<int64_t>(key0) * D,
                                                     static_cast<uint32_t>(rows * D)),
                        buffer_rsrc(vbase + key0 * vs_b, static_cast<uint32_t>(rows * vs_b)));
@@ -636,24 +754,34 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
   // are the entries [e_begin, e_split); the tiered walk takes them first with
   // fp8 Q only, then reloads bf16 Q for the rest, so the two copies of Q are
   // never held together.
-  int e_split = e_begin;
+  // Likewise the fp4 tiles are a prefix [e_begin, e_split4) of it, and the
+  // fp8 ones [e_split4, e_split) follow.
+  int e_split = e_begin, e_split4 = e_begin;
   if constexpr (kTiers) {
     for (int e0 = e_begin; e0 < e_end; e0 += 64) {
       const int e = e0 + lane;
-      const uint64_t bits = __ballot(e < e_end && is_low(a.k_tile[e]));
+      const int kt = e < e_end ? a.k_tile[e] : 0;
+      const uint64_t bits = __ballot(e < e_end && (is_low(kt) || is_fp4(kt)));
+      const uint64_t bits4 = __ballot(e < e_end && is_fp4(kt));
       e_split += __popcll(bits);
+      e_split4 += __popcll(bits4);
       if (~bits != 0) break;
     }
   }
 
-  // Walks the kept tiles in 32-key halves: entries [e_begin, e_split) with
-  // low_half, then at_split(), then [e_split, e_end) with high_half; each half
-  // callback is called as half(stage, key0, kb, partial).
-  auto walk = [&](auto&& low_half, auto&& at_split, auto&& high_half) {
+  // tier of list entry e (2: fp4, 1: fp8, 0: bf16)
+  auto tier_of = [&](int e) __attribute__((always_inline)) -> int { return e < e_split4 ? 2 : (e < e_split ? 1 : 0); };
+
+  // Walks the kept tiles in 32-key halves: entries [e_begin, e_split4) with
+  // fp4_half, [e_split4, e_split) with low_half, then at_split(), then
+  // [e_split, e_end) with high_half; each half callback is called as
+  // half(stage, key0, kb, partial).
+  auto walk = [&](auto&& fp4_half, auto&& low_half, auto&& at_split, auto&& high_half) __attribute__((always_inline)) {
     load_list(e_begin);
-    if (e_begin < e_end) dma(smem, tile_of(e_begin), 0, e_begin < e_split);
+    if (e_begin < e_end) dma(smem, tile_of(e_begin), 0, tier_of(e_begin));
     int cur = 0;  // byte offset of the stage holding the current half
-    auto run = [&](int e_lo, int e_hi, bool low, auto&& half) {
+    // tier: of the phase's halves; a prefetch takes min(tier, the next entry's)
+    auto run = [&](int e_lo, int e_hi, int tier, auto&& half) __attribute__((always_inline)) {
       for (int e = e_lo; e < e_hi; ++e) {
         const int kt = tile_of(e);
         const bool partial = partial_of(e, kt);
@@ -662,37 +790,49 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
           wait_vmcnt0();    // this wave's copies of this half have landed
           __syncthreads();  // ... and every wave's; all reads of the other stage are done
           if (kb == 0) {
-            dma(smem + (cur ^ C::kStageBytes), kt, 1, low);
+            dma(smem + (cur ^ C::kStageBytes), kt, 1, tier);
           } else if (e + 1 < e_end) {
             if (e + 1 - list_e0 == 64) load_list(e + 1);
-            dma(smem + (cur ^ C::kStageBytes), tile_of(e + 1), 0, low && e + 1 < e_split);
+            dma(smem + (cur ^ C::kStageBytes), tile_of(e + 1), 0, min(tier, tier_of(e + 1)));
           }
           half(smem + cur, kt * kBlockK, kb, partial);
           cur ^= C::kStageBytes;
         }
       }
     };
-    if constexpr (kTiers) {
-      run(e_begin, e_split, true, low_half);
+    if constexpr (kTiers >= 2) {
+      run(e_begin, e_split4, 2, fp4_half);
+      load_q();  // fp4 -> fp8: fp8 Q from a fresh bf16 Q
+      make_q8();
+    }
+    if constexpr (kTiers >= 1) {
+      run(e_split4, e_split, 1, low_half);
       at_split();
     }
-    run(e_split, e_end, false, high_half);
+    run(e_split, e_end, 0, high_half);
     __syncthreads();  // all reads of the last stage are done before another walk refills it
   };
   // score scale of the LOW half starting at key0: s_q times the fp8 K scale
   // of that half (kept positive so that 0 * -inf never arises: a zero scale
   // means all-zero codes, whose scores are 0 at any positive scale)
-  auto low_sc = [&](int key0) -> float {
+  auto low_sc = [&](int key0) __attribute__((always_inline)) -> float {
     if constexpr (kTiers) return fmaxf(st.s_q * k8scale[key0 / kHalf], 1.17549435e-38f);
     return 1.0f;
   };
-  auto attend_low = [&](const char LDS_AS* stage, int key0, int kb, bool partial) {
+  auto fp4_sc = [&](int key0) __attribute__((always_inline)) -> float {
+    if constexpr (kTiers >= 2) return fmaxf(st.s_q4 * k4scale[key0 / kHalf], 1.17549435e-38f);
+    return 1.0f;
+  };
+  auto attend_fp4 = [&](const char LDS_AS* stage, int key0, int kb, bool partial) __attribute__((always_inline)) {
+    K::compute_half(stage, ln, st, kb, key0, partial, c_log2, need_ref, true, fp4_sc(key0 + kb * kHalf), true);
+  };
+  auto attend_low = [&](const char LDS_AS* stage, int key0, int kb, bool partial) __attribute__((always_inline)) {
     K::compute_half(stage, ln, st, kb, key0, partial, c_log2, need_ref, true, low_sc(key0 + kb * kHalf));
   };
-  auto attend = [&](const char LDS_AS* stage, int key0, int kb, bool partial) {
+  auto attend = [&](const char LDS_AS* stage, int key0, int kb, bool partial) __attribute__((always_inline)) {
     K::compute_half(stage, ln, st, kb, key0, partial, c_log2, need_ref);
   };
-  auto clear = [&]() {
+  auto clear = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::kOBlocks; ++i)
 #pragma unroll
@@ -700,14 +840,11 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
     st.l = 0.0f;
     st.lb = 0.0f;
   };
-  auto reload_q = [&]() {
+  auto reload_q = [&]() __attribute__((always_inline)) {
     if constexpr (kTiers) load_q();
   };
-  auto requant_q = [&]() {
-    if constexpr (kTiers) {
-      load_q();
-      make_q8();
-    }
+  auto requant_q = [&]() __attribute__((always_inline)) {
+    if constexpr (kTiers) first_q();
   };
 
   // Usual case: one walk with a fixed reference per row.  Every P of a row is
@@ -715,14 +852,17 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
   // walk again for the exact row maxima and once more with them as the
   // reference (then every P <= 1).
   clear();
-  walk(attend_low, reload_q, attend);
+  walk(attend_fp4, attend_low, reload_q, attend);
   if (__syncthreads_or(!(st.l <= kSumLimit))) {
     requant_q();
-    walk([&](const char LDS_AS* stage, int key0, int kb, bool partial) {
+    walk([&](const char LDS_AS* stage, int key0, int kb, bool partial) __attribute__((always_inline)) {
+           K::max_half(stage, ln, st, kb, key0, partial, true, fp4_sc(key0 + kb * kHalf), true);
+         },
+         [&](const char LDS_AS* stage, int key0, int kb, bool partial) __attribute__((always_inline)) {
            K::max_half(stage, ln, st, kb, key0, partial, true, low_sc(key0 + kb * kHalf));
          },
          reload_q,
-         [&](const char LDS_AS* stage, int key0, int kb, bool partial) {
+         [&](const char LDS_AS* stage, int key0, int kb, bool partial) __attribute__((always_inline)) {
            K::max_half(stage, ln, st, kb, key0, partial);
          });
     st.m = st.mt;
@@ -730,7 +870,7 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
     need_ref = false;
     clear();
     requant_q();
-    walk(attend_low, reload_q, attend);
+    walk(attend_fp4, attend_low, reload_q, attend);
   }
 
   // epilogue
@@ -787,7 +927,7 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
   }
 }
 
-template <int D, bool kOutBf16, bool kCausal, bool kTiers = false>
+template <int D, bool kOutBf16, bool kCausal, int kTiers = 0>
 int launch_t(const AttnLaunch& a, hipStream_t stream) {
   hipLaunchKernelGGL((attn_fwd_kernel<D, kOutBf16, kCausal, kTiers>),
                      dim3(static_cast<unsigned>(a.sched.grid)), dim3(kThreads), 0, stream, a);
@@ -798,7 +938,8 @@ int launch_t(const AttnLaunch& a, hipStream_t stream) {
 
 template <int D>
 int launch_d(const AttnLaunch& a, hipStream_t stream) {
-  if (a.k8) return a.o_bf16 ? launch_t<D, true, false, true>(a, stream) : launch_t<D, false, false, true>(a, stream);
+  if (a.k4) return a.o_bf16 ? launch_t<D, true, false, 2>(a, stream) : launch_t<D, false, false, 2>(a, stream);
+  if (a.k8) return a.o_bf16 ? launch_t<D, true, false, 1>(a, stream) : launch_t<D, false, false, 1>(a, stream);
   if (a.o_bf16) return a.causal ? launch_t<D, true, true>(a, stream) : launch_t<D, true, false>(a, stream);
   return a.causal ? launch_t<D, false, true>(a, stream) : launch_t<D, false, false>(a, stream);
 }

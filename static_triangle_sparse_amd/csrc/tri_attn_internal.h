@@ -167,6 +167,11 @@ struct AttnLaunch {
   const void* k8;
   const float* k8_scale;
   const int32_t* head_low_dist;
+  // fp4 tier (NULL k4 = off): fp4 K [B, Hkv, N, d / 2 bytes], its scales, and
+  // the per-head fp4 boundary (tiles at or beyond it are scored in fp4)
+  const void* k4;
+  const float* k4_scale;
+  const int32_t* head_fp4_dist;
   // split of heavy tiles (sched.n_split > 1): chunk items write unnormalised
   // partials, item = ((b * heads_q + h) * n_heavy + (n_qtiles - 1 - t)) *
   // n_split + c: O [item][128][d] f32 and (m, l, lb) [item][3][128] f32
@@ -229,7 +234,8 @@ struct QuantLaunch {
   int64_t k_stride[3];
   int32_t heads_kv, head_dim, seqlen;
   int64_t n_blocks;  // batch * heads_kv * ceil(N / 32)
-  void* k8;          // out: fp8 [B, Hkv, N, d bytes]
+  int32_t fp4;       // 0: fp8 copy (d bytes per row), 1: fp4 copy (d / 2 bytes per row)
+  void* k8;          // out: fp8 [B, Hkv, N, d bytes] or fp4 [B, Hkv, N, d / 2 bytes]
   float* scale;      // out: [B, Hkv, ceil(N / 32)]
 };
 

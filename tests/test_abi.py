@@ -27,11 +27,12 @@ def test_header_symbols_are_exported():
             "tri_attn_last_error", "tri_dyn_plan_sizes", "tri_dyn_plan",
             "tri_attn_prefill_lists", "tri_attn_plan_heads", "tri_attn_prefill_heads",
             "tri_attn_quantize_k_sizes", "tri_attn_quantize_k", "tri_attn_prefill_tiered",
-            "tri_attn_split_workspace_size", "tri_attn_prefill_split", "tri_attn_split_work_item"} <= set(names)
+            "tri_attn_split_workspace_size", "tri_attn_prefill_split", "tri_attn_split_work_item",
+            "tri_attn_quantize_k4_sizes", "tri_attn_quantize_k4"} <= set(names)
     lib = ctypes.CDLL(_abi.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert tsa.tri_attn_abi_version() == 2
+    assert tsa.tri_attn_abi_version() == 3
 
 
 # ----------------------------------------------------------- plan validation
@@ -420,6 +421,14 @@ def test_quantize_k_sizes_and_arguments():
     assert lib.tri_attn_quantize_k(ctypes.byref(bad), dev, dev, None) == tsa.TRI_ERR_UNSUPPORTED
     z = _good_tensors(N=0)
     assert lib.tri_attn_quantize_k(ctypes.byref(z), dev, dev, None) == tsa.TRI_OK
+    # the fp4 copy: half the bytes, the same scales
+    assert lib.tri_attn_quantize_k4_sizes(ctypes.byref(t), ctypes.byref(nb), ctypes.byref(ns)) == tsa.TRI_OK
+    assert nb.value == 2 * 2 * 1000 * 64 and ns.value == 2 * 2 * 32
+    assert tsa.tri_attn_quantize_k4_sizes(t) == (nb.value, ns.value)
+    assert lib.tri_attn_quantize_k4(ctypes.byref(t), None, dev, None) == tsa.TRI_ERR_INVALID
+    assert lib.tri_attn_quantize_k4(ctypes.byref(t), dev + 8, dev, None) == tsa.TRI_ERR_INVALID
+    assert lib.tri_attn_quantize_k4(ctypes.byref(bad), dev, dev, None) == tsa.TRI_ERR_UNSUPPORTED
+    assert lib.tri_attn_quantize_k4(ctypes.byref(z), dev, dev, None) == tsa.TRI_OK
 
 
 def test_prefill_tiered_rejects_bad_arguments():
@@ -427,15 +436,20 @@ def test_prefill_tiered_rejects_bad_arguments():
     t = _good_tensors(B=1, Hq=4, Hkv=2, N=1000, d=128)
     mp = tsa.mask_params(1000, "triangle", 16, 128, 64)
     dev = 1 << 24
-    good = [dev, dev, dev, dev, dev, dev]   # low_dist, k8, scale, row_ptr, k_tile, flags
+    # low_dist, k8, scale, fp4_dist, k4, scale4, row_ptr, k_tile, flags
+    good = [dev, dev, dev, dev, dev, dev, dev, dev, dev]
 
     def call(mp_, args):
         return lib.tri_attn_prefill_tiered(ctypes.byref(t), ctypes.byref(mp_), *args, None)
-    for i in range(6):
+    for i in (0, 1, 2, 6, 7, 8):
         args = list(good)
         args[i] = None
         assert call(mp, args) == tsa.TRI_ERR_INVALID, i
-    for i, off in ((0, 2), (1, 8), (2, 2), (3, 2), (4, 2)):   # int32 4-byte, fp8 K 16-byte
+    for i in (3, 4, 5):   # the fp4 arrays go together
+        args = list(good)
+        args[i] = None
+        assert call(mp, args) == tsa.TRI_ERR_INVALID, i
+    for i, off in ((0, 2), (1, 8), (2, 2), (3, 2), (4, 8), (5, 2), (6, 2), (7, 2)):   # int32/f32 4, K copies 16
         args = list(good)
         args[i] = dev + off
         assert call(mp, args) == tsa.TRI_ERR_INVALID, i
@@ -447,3 +461,5 @@ def test_prefill_tiered_rejects_bad_arguments():
     z = _good_tensors(N=0)
     mz = tsa.mask_params(0, "triangle", 16, 128, 64)
     assert lib.tri_attn_prefill_tiered(ctypes.byref(z), ctypes.byref(mz), *good, None) == tsa.TRI_OK
+    no4 = good[:3] + [None, None, None] + good[6:]
+    assert lib.tri_attn_prefill_tiered(ctypes.byref(z), ctypes.byref(mz), *no4, None) == tsa.TRI_OK
