@@ -290,32 +290,45 @@ def bench_per_head(t, args, cfg, d, Hq, B, dev, stream):
 
 def bench_tiered(t, args, cfg, plan, tri_ms, d, Hq, B, dev, stream):
     """The triangle layer with precision tiers (TriAttention page: per-head
-    diagonal-distance boundaries choose each tile's precision): key tiles at
-    least --low-dist keys behind the query tile scored in fp8 (e4m3), the
-    rest in bf16.  K's fp8 copy and the layer are timed separately."""
+    diagonal-distance boundaries choose each tile's precision, 4-bit and 8-bit
+    tiers): key tiles at least --low-dist keys behind the query tile scored in
+    fp8 (e4m3), the rest in bf16; then two settings with the fp4 (e2m1) tier.
+    The fp8 and fp4 copies of K and the layer are timed separately."""
     import numpy as np
     import torch
     import static_triangle_sparse_amd as tsa
-    qk = tsa.QuantizedK(t, dev)
+    qk = tsa.QuantizedK(t, dev, fp4=True)
     quant_ms, _ = time_launches(lambda: qk.run(t, stream), args.dense_steps, 1)
-    dist = np.full(Hq, args.low_dist, np.int32)
-    d_dist = torch.from_numpy(dist).to(dev)
-    run = lambda: tsa.tri_attn_prefill_tiered(t, plan.mp, d_dist.data_ptr(), qk.k8.data_ptr(),
-                                              qk.scale.data_ptr(), plan.d_row_ptr.data_ptr(),
-                                              plan.d_k_tile.data_ptr(), plan.d_flags.data_ptr(), stream)
-    ms, _ = time_launches(run, args.steps, args.warmup)
     rows = np.repeat(np.arange(plan.row_ptr.size - 1), np.diff(plan.row_ptr))
-    n_low = int(np.sum(rows * 128 - (plan.k_tile.astype(np.int64) * 64 + 63) >= args.low_dist))
-    frac = n_low / max(1, plan.k_tile.size)
+    dist_min = rows * 128 - (plan.k_tile.astype(np.int64) * 64 + 63)
+
+    def layer(low_dist, fp4_dist=None):
+        d8 = torch.from_numpy(np.full(Hq, low_dist, np.int32)).to(dev)
+        d4 = None if fp4_dist is None else torch.from_numpy(np.full(Hq, fp4_dist, np.int32)).to(dev)
+        f4 = (None, None, None) if d4 is None else (d4.data_ptr(), qk.k4.data_ptr(), qk.scale4.data_ptr())
+        run = lambda: tsa.tri_attn_prefill_tiered(t, plan.mp, d8.data_ptr(), qk.k8.data_ptr(), qk.scale.data_ptr(),
+                                                  *f4, plan.d_row_ptr.data_ptr(), plan.d_k_tile.data_ptr(),
+                                                  plan.d_flags.data_ptr(), stream)
+        ms, _ = time_launches(run, args.steps, args.warmup)
+        n4 = int(np.sum(dist_min >= fp4_dist)) if fp4_dist is not None else 0
+        n8 = int(np.sum(dist_min >= low_dist)) - (int(np.sum((dist_min >= low_dist) & (dist_min >= fp4_dist)))
+                                                  if fp4_dist is not None else 0)
+        return {"fp8_from": low_dist, "fp4_from": fp4_dist, "ms": round(ms, 4),
+                "fp8_tile_fraction": round(n8 / max(1, plan.k_tile.size), 4),
+                "fp4_tile_fraction": round(n4 / max(1, plan.k_tile.size), 4),
+                "speedup_vs_bf16_triangle": round(tri_ms / ms, 3)}
     flops = 4.0 * 128 * 64 * d * plan.k_tile.size * Hq * B
-    tf = flops / (ms * 1e-3) / 1e12
-    print(f"[bench] tiered triangle (fp8 scores from distance {args.low_dist}): K to fp8 "
-          f"{quant_ms:.3f} ms + layer {ms:.3f} ms, {100 * frac:.1f}% of tiles fp8",
+    main_ = layer(args.low_dist)
+    main_["kept_tflops"] = round(flops / (main_["ms"] * 1e-3) / 1e12, 2)
+    three = [layer(0, 1024), layer(10 ** 6, 0)]
+    print(f"[bench] tiered triangle (fp8 scores from distance {args.low_dist}): K to fp8 + fp4 "
+          f"{quant_ms:.3f} ms, layer {main_['ms']:.3f} ms ({main_['speedup_vs_bf16_triangle']}x); "
+          f"fp8 near / fp4 from 1024: {three[0]['ms']:.3f} ms; fp4 off the diagonal band: {three[1]['ms']:.3f} ms",
           file=sys.stderr, flush=True)
-    return {"low_dist": args.low_dist, "low_tile_fraction": round(frac, 4),
-            "quantize_ms": round(quant_ms, 4), "attention_ms": round(ms, 4),
-            "kept_tflops": round(tf, 2), "speedup_vs_bf16_triangle": round(tri_ms / ms, 3),
-            "speedup_incl_quantize": round(tri_ms / (ms + quant_ms), 3)}
+    return {"low_dist": args.low_dist, "low_tile_fraction": main_["fp8_tile_fraction"],
+            "quantize_fp8_fp4_ms": round(quant_ms, 4), "attention_ms": main_["ms"],
+            "kept_tflops": main_["kept_tflops"], "speedup_vs_bf16_triangle": main_["speedup_vs_bf16_triangle"],
+            "with_fp4_tier": three}
 
 
 def main(argv=None):
