@@ -30,6 +30,14 @@
 //      with the transposing LDS read ds_read_b64_tr_b16.
 // Output O = acc / sum(bf16 P) (stored bf16 round-to-nearest-even or f32) and
 // the natural-log LSE = scale * m + ln sum(P) are written once per row.
+//
+// Variants of the same walk:
+//   * list rows per (batch, head) for per-head boundaries and dynamic lists;
+//   * chunks of a split last-Q row, which leave unnormalised partials for
+//     the merge kernel instead of O and LSE;
+//   * precision tiers (TriAttention page): the far tiles of a list are a
+//     prefix of it, scored from fp4 and/or fp8 copies of Q and K on the
+//     scaled MFMA before the bf16 tiles; the tier count is a template value.
 #include <hip/hip_runtime.h>
 #include <limits.h>
 #include <stdint.h>
@@ -226,14 +234,34 @@ template <int D, int kTiers>
 struct TierLane {};
 template <int D>
 struct TierLane<D, 1> {
-  uint32_t k8_dma[Cfg<D>::kK8BlocksPerWave];
   int k8_rd;
 };
 template <int D>
 struct TierLane<D, 2> : TierLane<D, 1> {
-  uint32_t k4_dma[Cfg<D>::kK4BlocksPerWave];
   int k4_rd;
 };
+
+// Lane id, materialized afresh where it is used: the copy offsets of the fp8
+// and fp4 K halves are recomputed at every copy from it rather than held in
+// registers.  Held over the loop, they were spilled, and every reload from
+// scratch waited (vmcnt, in order) for all copies in flight.  The volatile
+// statement keeps the compiler from hoisting the computation out of the loop.
+__device__ __forceinline__ int lane_id_fresh() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// Global byte offset (within the half) of the 16-byte chunk that lands at
+// byte x of an LDS half stored as 32 rows of `stride` bytes holding `row_bytes`
+// bytes each; chunks on row padding re-read chunk 0 of their row.
+template <int kStride, int kRowBytes>
+__device__ __forceinline__ uint32_t padded_dma_offset(int x) {
+  const int row = x / kStride;
+  int chunk = (x - row * kStride) / 16;
+  if (chunk >= kRowBytes / 16) chunk = 0;
+  return static_cast<uint32_t>(min(row, kHalf - 1) * kRowBytes + chunk * 16);
+}
 
 template <int D, bool kOutBf16, bool kCausal, int kTiers>
 struct Kernel {
@@ -284,11 +312,12 @@ struct Kernel {
   static __device__ __forceinline__ void issue_dma_low(char LDS_AS* stage, const Lane& ln, int wave,
                                                        const u32x4& k8_rsrc, const u32x4& v_rsrc) {
     if constexpr (kTiers) {
+      const int l16 = lane_id_fresh() * 16;
 #pragma unroll
       for (int i = 0; i < C::kK8BlocksPerWave; ++i) {
         const int blk = i * kWaves + wave;
         if (C::kK8Blocks % kWaves == 0 || blk < C::kK8Blocks)
-          lds_dma16(k8_rsrc, ln.k8_dma[i], stage + blk * 1024);
+          lds_dma16(k8_rsrc, padded_dma_offset<C::kK8Stride, D>(blk * 1024 + l16), stage + blk * 1024);
       }
 #pragma unroll
       for (int i = 0; i < C::kVBlocksPerWave; ++i) {
@@ -303,11 +332,12 @@ struct Kernel {
   static __device__ __forceinline__ void issue_dma_fp4(char LDS_AS* stage, const Lane& ln, int wave,
                                                        const u32x4& k4_rsrc, const u32x4& v_rsrc) {
     if constexpr (kTiers >= 2) {
+      const int l16 = lane_id_fresh() * 16;
 #pragma unroll
       for (int i = 0; i < C::kK4BlocksPerWave; ++i) {
         const int blk = i * kWaves + wave;
         if (C::kK4Blocks % kWaves == 0 || blk < C::kK4Blocks)
-          lds_dma16(k4_rsrc, ln.k4_dma[i], stage + blk * 1024);
+          lds_dma16(k4_rsrc, padded_dma_offset<C::kK4Stride, D / 2>(blk * 1024 + l16), stage + blk * 1024);
       }
 #pragma unroll
       for (int i = 0; i < C::kVBlocksPerWave; ++i) {
@@ -552,14 +582,6 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
     k8scale = a.k8_scale + bg * ((N + kHalf - 1) / kHalf);
     low_dist = a.head_low_dist[w.h];
     ln.k8_rd = l32 * C::kK8Stride + ln.hi * 32;
-#pragma unroll
-    for (int i = 0; i < C::kK8BlocksPerWave; ++i) {
-      const int x = (i * kWaves + wave) * 1024 + lane * 16;
-      const int row = x / C::kK8Stride;
-      int chunk = (x - row * C::kK8Stride) / 16;
-      if (chunk >= D / 16) chunk = 0;  // row padding: re-read chunk 0 (never used)
-      ln.k8_dma[i] = static_cast<uint32_t>(min(row, kHalf - 1) * D + chunk * 16);
-    }
   }
   // fp4 tier (optional): rows of D / 2 bytes; a tile is fp4 when
   // q0 - (64 kt + 63) >= this head's fp4 boundary (the farthest tier wins)
@@ -574,14 +596,6 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
       fp4_dist = a.head_fp4_dist[w.h];
     }
     ln.k4_rd = l32 * C::kK4Stride + ln.hi * 16;
-#pragma unroll
-    for (int i = 0; i < C::kK4BlocksPerWave; ++i) {
-      const int x = (i * kWaves + wave) * 1024 + lane * 16;
-      const int row = x / C::kK4Stride;
-      int chunk = (x - row * C::kK4Stride) / 16;
-      if (chunk >= D / 32) chunk = 0;  // row padding: re-read chunk 0 (never used)
-      ln.k4_dma[i] = static_cast<uint32_t>(min(row, kHalf - 1) * (D / 2) + chunk * 16);
-    }
   }
   auto is_low = [&](int kt) __attribute__((always_inline)) -> bool { return kTiers && q0 - (kt * kBlockK + kBlockK - 1) >= low_dist; };
   auto is_fp4 = [&](int kt) __attribute__((always_inline)) -> bool { return kTiers >= 2 && q0 - (kt * kBlockK + kBlockK - 1) >= fp4_dist; };
