@@ -60,6 +60,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 #define LDS_AS __attribute__((address_space(3)))
+// Read-only data read at uniform addresses inside the tile loop (the fp8 and
+// fp4 K scales): through the constant address space such loads are scalar
+// (s_load, counted on lgkmcnt).  As vector loads they were counted on vmcnt,
+// in order with the LDS-DMA copies, and waiting for one waited for the copies
+// of the next half in flight.
+#define CONST_AS __attribute__((address_space(4)))
 #define GLOBAL_AS __attribute__((address_space(1)))
 
 constexpr int kBlockQ = TRI_KERNEL_BLOCK_Q;  // 128 query rows per workgroup
@@ -574,25 +580,25 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
   // tiered kernel: fp8 K rows of D bytes per (batch, KV head); the LOW test
   // of key tile kt is q0 - (64 kt + 63) >= this head's boundary
   const char* k8base = nullptr;
-  const float* k8scale = nullptr;
+  const CONST_AS float* k8scale = nullptr;
   int low_dist = 0;
   if constexpr (kTiers) {
     const int64_t bg = static_cast<int64_t>(w.b) * a.sched.heads_kv + g;
     k8base = static_cast<const char*>(a.k8) + bg * N * D;
-    k8scale = a.k8_scale + bg * ((N + kHalf - 1) / kHalf);
+    k8scale = reinterpret_cast<const CONST_AS float*>(reinterpret_cast<uintptr_t>(a.k8_scale)) + bg * ((N + kHalf - 1) / kHalf);
     low_dist = a.head_low_dist[w.h];
     ln.k8_rd = l32 * C::kK8Stride + ln.hi * 32;
   }
   // fp4 tier (optional): rows of D / 2 bytes; a tile is fp4 when
   // q0 - (64 kt + 63) >= this head's fp4 boundary (the farthest tier wins)
   const char* k4base = nullptr;
-  const float* k4scale = nullptr;
+  const CONST_AS float* k4scale = nullptr;
   int fp4_dist = INT_MAX;
   if constexpr (kTiers >= 2) {
     {
       const int64_t bg = static_cast<int64_t>(w.b) * a.sched.heads_kv + g;
       k4base = static_cast<const char*>(a.k4) + bg * N * (D / 2);
-      k4scale = a.k4_scale + bg * ((N + kHalf - 1) / kHalf);
+      k4scale = reinterpret_cast<const CONST_AS float*>(reinterpret_cast<uintptr_t>(a.k4_scale)) + bg * ((N + kHalf - 1) / kHalf);
       fp4_dist = a.head_fp4_dist[w.h];
     }
     ln.k4_rd = l32 * C::kK4Stride + ln.hi * 16;
