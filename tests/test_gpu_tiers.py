@@ -287,3 +287,20 @@ def test_llama_128k_three_tiers_sampled(dev):
                                   kw["last_q"], [0], rows=rows, dist4=[1024])
         idx = torch.from_numpy(rows).to(dev)
         gu.check(o[:, h:h + 1][:, :, idx], lse[:, h:h + 1][:, :, idx], ro, rl, f"128K three tiers head {h}")
+
+
+def test_three_tiers_batched(dev):
+    # batch entries address the fp8 / fp4 copies and scales by (batch, KV head)
+    gu.note("three tiers, batch 2, N=600, d=64")
+    B, Hq, Hkv, N, d = 2, 4, 2, 600, 64
+    bits, (q, k, v) = gu.make_inputs(97, B, Hq, Hkv, N, d, dev)
+    qk = tsa.quantize_k(q, k, fp4=True)
+    o = torch.full((B, Hq, N, d), float("nan"), dtype=torch.float32, device=dev)
+    lse = torch.full((B, Hq, N), float("nan"), dtype=torch.float32, device=dev)
+    dist8, dist4 = [0, 64, 128, 10 ** 6], [256, 10 ** 6, 128, 0]
+    tsa.prefill(q, k, v, mode="tiered", sink=32, window=256, last_q=64, plan=qk, low_dist=dist8,
+                fp4_dist=dist4, o_dtype=torch.float32, out=o, lse=lse)
+    torch.cuda.synchronize()
+    qf, kf, vf = (gu.as_f64(x) for x in bits)
+    ro, rl = otiers.attention(qf, kf, vf, 32, 256, 64, dist8, dist4=dist4)
+    gu.check(o, lse, ro, rl, "three tiers batched")
