@@ -402,12 +402,22 @@ struct Kernel {
       }
     }
     if (!done) {
+      // Four K operand reads run ahead of the dependent MFMA chain: four
+      // reads first, then each MFMA followed by the next read.  Without the
+      // schedule groups the allocator keeps only two in flight.
       const char LDS_AS* kp = stage + ln.k_rd;
+      bf16x8 kv[C::kQSteps];
 #pragma unroll
-      for (int q = 0; q < C::kQSteps; ++q) {
-        const bf16x8 kv = *reinterpret_cast<const LDS_AS bf16x8*>(kp + q * 32);
-        s = mfma32(kv, st.q[q], s);
+      for (int q = 0; q < C::kQSteps; ++q) kv[q] = *reinterpret_cast<const LDS_AS bf16x8*>(kp + q * 32);
+#pragma unroll
+      for (int q = 0; q < C::kQSteps; ++q) s = mfma32(kv[q], st.q[q], s);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
+#pragma unroll
+      for (int q = 0; q < C::kQSteps - 4; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // the last 4 MFMAs
     }
     if (partial) {
       mfma_result_fence(s);  // the masking below reads the MFMA result in assembly
@@ -495,6 +505,10 @@ struct Kernel {
         rb[kc] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rb[kc], false);
       }
     st.lb += rb[0] + rb[1];
+    // Keep both sums here: left alone, the compiler sinks them past the PV
+    // product into the next half, so the 16 fp32 P registers stay live
+    // across it and the V reads below run one MFMA ahead instead of four.
+    asm volatile("" : "+v"(st.l), "+v"(st.lb));
 
     // O^T += V^T . P^T ; V^T operand from two transposing reads per 16-key step
     const char LDS_AS* vp = stage + C::kKBytes + ln.v_rd;
