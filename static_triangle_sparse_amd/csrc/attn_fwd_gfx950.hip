@@ -478,8 +478,9 @@ struct Kernel {
     // P = exp2(s c - m c) as packed bf16; 16-key step kc = registers 8 kc .. 8 kc + 7.
     // Two row sums: of the fp32 P for the LSE, and of the bf16 P the PV
     // product actually uses (v_dot2_f32_bf16) to normalise O, so that the
-    // output weights sum to one exactly.  Pairwise trees keep the dependent
-    // chains short.
+    // output weights sum to one exactly.  The fp32 sum is a pairwise tree;
+    // the bf16 sum is one v_dot2 chain seeded with the running sum (no
+    // separate partials to initialise and add).
     bf16x8 pb[2];
     float pf[16];
 #pragma unroll
@@ -495,16 +496,14 @@ struct Kernel {
 #pragma unroll
     for (int r = 0; r < 4; ++r) pf[r] += pf[r + 4];
     st.l += (pf[0] + pf[2]) + (pf[1] + pf[3]);
-    float rb[2] = {0.0f, 0.0f};
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const bf16x2 pr = {pb[kc][2 * x], pb[kc][2 * x + 1]};
-        rb[kc] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rb[kc], false);
+        st.lb = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, st.lb, false);
       }
-    st.lb += rb[0] + rb[1];
     // Keep both sums here: left alone, the compiler sinks them past the PV
     // product into the next half, so the 16 fp32 P registers stay live
     // across it and the V reads below run one MFMA ahead instead of four.
