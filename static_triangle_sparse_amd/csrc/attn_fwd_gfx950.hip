@@ -552,6 +552,9 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // the range is lost through readfirstlane; with it the copy loops below
+  // drop the guards of the blocks every wave has
+  __builtin_assume(wave >= 0 && wave < kWaves);
   const int N = a.seqlen;
   const int g = w.h / a.sched.group;
   const int q0 = w.t * kBlockQ;
