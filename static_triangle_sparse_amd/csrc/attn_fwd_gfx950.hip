@@ -510,6 +510,10 @@ struct Kernel {
     asm volatile("" : "+v"(st.l), "+v"(st.lb));
 
     // O^T += V^T . P^T ; V^T operand from two transposing reads per 16-key step
+    // The PV product runs at raised wave priority: while one wave issues
+    // its MFMAs, the other waves of the SIMD fill the gaps with their
+    // softmax work instead of holding the MFMA-ready wave back.
+    __builtin_amdgcn_s_setprio(1);
     const char LDS_AS* vp = stage + C::kKBytes + ln.v_rd;
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
@@ -526,6 +530,7 @@ struct Kernel {
         const u32x4 w = {w0[0], w0[1], w1[0], w1[1]};
         st.o[ob] = mfma32(__builtin_bit_cast(bf16x8, w), pb[kc], st.o[ob]);
       }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // Exact-max pass over one 32-key half: scores and row max only.
