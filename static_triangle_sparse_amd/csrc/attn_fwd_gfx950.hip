@@ -42,8 +42,6 @@
 #include <limits.h>
 #include <stdint.h>
 
-#include <utility>
-
 #include "tri_attn_internal.h"
 
 namespace triattn {
@@ -152,24 +150,40 @@ __device__ __forceinline__ uint32_t low_bits(int x) {
   return r;
 }
 
-// s, or -inf where bit O of `drop` is set: a sign-extended one-bit field
-// selects the -inf pattern bit by bit (two full-rate instructions instead of
-// a compare and a select).
-template <int O>
-__device__ __forceinline__ float drop_if(float s, uint32_t drop, uint32_t neg_inf_bits) {
-  uint32_t m, r = __float_as_uint(s);
-  asm("v_bfe_i32 %0, %2, %3, 1\n\t"
-      "v_bfi_b32 %1, %0, %4, %1"
-      : "=&v"(m), "+v"(r)
-      : "v"(drop), "i"(O), "s"(neg_inf_bits));
-  return __uint_as_float(r);
-}
-
+// Each score s becomes -inf where its bit of `drop` is set: a sign-extended
+// one-bit field selects the -inf pattern bit by bit (two full-rate
+// instructions instead of a compare and a select).
 // Register r of a score block holds key offset 8 (r >> 2) + (r & 3) (+ 4 for
-// the upper half-wave, removed by the caller's shift of `drop`).
-template <int... R>
-__device__ __forceinline__ void drop_keys(float (&s)[16], uint32_t drop, std::integer_sequence<int, R...>) {
-  ((s[R] = drop_if<(R >> 2) * 8 + (R & 3)>(s[R], drop, kNegInfBits)), ...);
+// the upper half-wave, removed by the caller's shift of `drop`).  One
+// assembly block for all 16 registers: as separate statements the compiler
+// put a wait state between every two of them.
+__device__ __forceinline__ void drop_keys(float (&s)[16], uint32_t drop) {
+  uint32_t u[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) u[r] = __float_as_uint(s[r]);
+  uint32_t m;
+  asm("v_bfe_i32 %16, %17, 0, 1\n\tv_bfi_b32 %0, %16, %18, %0\n\t"
+      "v_bfe_i32 %16, %17, 1, 1\n\tv_bfi_b32 %1, %16, %18, %1\n\t"
+      "v_bfe_i32 %16, %17, 2, 1\n\tv_bfi_b32 %2, %16, %18, %2\n\t"
+      "v_bfe_i32 %16, %17, 3, 1\n\tv_bfi_b32 %3, %16, %18, %3\n\t"
+      "v_bfe_i32 %16, %17, 8, 1\n\tv_bfi_b32 %4, %16, %18, %4\n\t"
+      "v_bfe_i32 %16, %17, 9, 1\n\tv_bfi_b32 %5, %16, %18, %5\n\t"
+      "v_bfe_i32 %16, %17, 10, 1\n\tv_bfi_b32 %6, %16, %18, %6\n\t"
+      "v_bfe_i32 %16, %17, 11, 1\n\tv_bfi_b32 %7, %16, %18, %7\n\t"
+      "v_bfe_i32 %16, %17, 16, 1\n\tv_bfi_b32 %8, %16, %18, %8\n\t"
+      "v_bfe_i32 %16, %17, 17, 1\n\tv_bfi_b32 %9, %16, %18, %9\n\t"
+      "v_bfe_i32 %16, %17, 18, 1\n\tv_bfi_b32 %10, %16, %18, %10\n\t"
+      "v_bfe_i32 %16, %17, 19, 1\n\tv_bfi_b32 %11, %16, %18, %11\n\t"
+      "v_bfe_i32 %16, %17, 24, 1\n\tv_bfi_b32 %12, %16, %18, %12\n\t"
+      "v_bfe_i32 %16, %17, 25, 1\n\tv_bfi_b32 %13, %16, %18, %13\n\t"
+      "v_bfe_i32 %16, %17, 26, 1\n\tv_bfi_b32 %14, %16, %18, %14\n\t"
+      "v_bfe_i32 %16, %17, 27, 1\n\tv_bfi_b32 %15, %16, %18, %15\n\t"
+      : "+v"(u[0]), "+v"(u[1]), "+v"(u[2]), "+v"(u[3]), "+v"(u[4]), "+v"(u[5]), "+v"(u[6]), "+v"(u[7]),
+        "+v"(u[8]), "+v"(u[9]), "+v"(u[10]), "+v"(u[11]), "+v"(u[12]), "+v"(u[13]), "+v"(u[14]), "+v"(u[15]),
+        "=&v"(m)
+      : "v"(drop), "s"(kNegInfBits));
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = __uint_as_float(u[r]);
 }
 
 // An MFMA result may be read by a VALU instruction only some wait states
@@ -429,7 +443,7 @@ struct Kernel {
       float sv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) sv[r] = s[r];
-      drop_keys(sv, drop, std::make_integer_sequence<int, 16>());
+      drop_keys(sv, drop);
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = sv[r];
     }
