@@ -378,8 +378,8 @@ struct Kernel {
   // A far half (fp4) is scored the same way from fp4 K and Q (format code 4
   // on both operands, 16 bytes per lane per 64-wide k-step).
   static __device__ __forceinline__ f32x16 scores(const char LDS_AS* stage, const Lane& ln, const State& st,
-                                                  int kb, int key0, bool partial, bool low = false,
-                                                  bool fp4 = false) {
+                                                  int kb, int key0, bool partial, uint32_t keep,
+                                                  bool low = false, bool fp4 = false) {
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.0f;
@@ -435,10 +435,7 @@ struct Kernel {
     }
     if (partial) {
       mfma_result_fence(s);  // the masking below reads the MFMA result in assembly
-      // bit o of `drop` is set when key base + o is masked for this lane's row
-      const int base = key0 + kb * 32;
-      const uint32_t keep = low_bits(ln.hi_lim - base + 1) &
-                            (low_bits(ln.sink_lim - base) | ~low_bits(ln.win_lo - base));
+      // bit o of `drop` is set when key 32 kb + o of the tile is masked for this lane's row
       const uint32_t drop = ~keep >> (ln.hi * 4);
       float sv[16];
 #pragma unroll
@@ -448,6 +445,11 @@ struct Kernel {
       for (int r = 0; r < 16; ++r) s[r] = sv[r];
     }
     return s;
+  }
+
+  // Bit o set when key base + o is kept for this lane's row (one 32-key half).
+  static __device__ __forceinline__ uint32_t keep_bits(const Lane& ln, int base) {
+    return low_bits(ln.hi_lim - base + 1) & (low_bits(ln.sink_lim - base) | ~low_bits(ln.win_lo - base));
   }
 
   // Row max over the 32 keys of a score block (16 here, 16 in lane ^ 32).
@@ -478,7 +480,12 @@ struct Kernel {
                                                       State& st, int kb, int key0, bool partial,
                                                       float c_log2, bool& need_ref, bool low = false,
                                                       float sc = 1.0f, bool fp4 = false) {
-    f32x16 s = scores(stage, ln, st, kb, key0, partial, low, fp4);
+    uint32_t keep = ~0u;
+    if (partial) {
+      keep = keep_bits(ln, key0 + kb * 32);
+      if (__ballot(keep != 0) == 0) return;  // no row of the wave keeps a key of this half
+    }
+    f32x16 s = scores(stage, ln, st, kb, key0, partial, keep, low, fp4);
     const float c = low ? c_log2 * sc : c_log2;
     if (need_ref) {
       // a row with no kept key so far has O = 0 and l = 0: its reference may still move
@@ -551,7 +558,12 @@ struct Kernel {
   static __device__ __forceinline__ void max_half(const char LDS_AS* stage, const Lane& ln, State& st, int kb,
                                                   int key0, bool partial, bool low = false, float sc = 1.0f,
                                                   bool fp4 = false) {
-    f32x16 s = scores(stage, ln, st, kb, key0, partial, low, fp4);
+    uint32_t keep = ~0u;
+    if (partial) {
+      keep = keep_bits(ln, key0 + kb * 32);
+      if (__ballot(keep != 0) == 0) return;
+    }
+    f32x16 s = scores(stage, ln, st, kb, key0, partial, keep, low, fp4);
     const float mx = row_max(s);
     st.mt = fmaxf(st.mt, low ? mx * sc : mx);
   }
