@@ -19,6 +19,7 @@
 //      registers for the whole loop).  Computing the transpose puts one query
 //      per lane, so row statistics are per-lane scalars;
 //   3. PARTIAL tiles apply the mask predicate per element, FULL tiles skip it;
+//      a half that no row of the wave keeps is skipped by that wave;
 //   4. softmax in fp32 with exp2 (log2 e folded into the scale) against a
 //      reference max that is fixed per row by the first block that keeps one
 //      of its keys, so the O accumulators are never rescaled in the loop; a
