@@ -883,12 +883,16 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
   // score scale of the LOW half starting at key0: s_q times the fp8 K scale
   // of that half (kept positive so that 0 * -inf never arises: a zero scale
   // means all-zero codes, whose scores are 0 at any positive scale)
+  // The second half of a last tile can start at or past N: it has no scale
+  // of its own (ceil(N / 32) per head), and all its keys are masked, so it
+  // reads the last one instead of the element past the array.
+  const int last_half = (N + kHalf - 1) / kHalf - 1;
   auto low_sc = [&](int key0) __attribute__((always_inline)) -> float {
-    if constexpr (kTiers) return fmaxf(st.s_q * k8scale[key0 / kHalf], 1.17549435e-38f);
+    if constexpr (kTiers) return fmaxf(st.s_q * k8scale[min(key0 / kHalf, last_half)], 1.17549435e-38f);
     return 1.0f;
   };
   auto fp4_sc = [&](int key0) __attribute__((always_inline)) -> float {
-    if constexpr (kTiers >= 2) return fmaxf(st.s_q4 * k4scale[key0 / kHalf], 1.17549435e-38f);
+    if constexpr (kTiers >= 2) return fmaxf(st.s_q4 * k4scale[min(key0 / kHalf, last_half)], 1.17549435e-38f);
     return 1.0f;
   };
   auto attend_fp4 = [&](const char LDS_AS* stage, int key0, int kb, bool partial) __attribute__((always_inline)) {
