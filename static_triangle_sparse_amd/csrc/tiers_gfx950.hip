@@ -32,12 +32,17 @@ constexpr int kHalfKeys = TRI_KERNEL_BLOCK_K / 2;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// One wave per (batch, KV head, half-tile), 4 per workgroup.  Lane l owns key
-// l / 2 of the block and output bytes [(l % 2) D / 2, (l % 2 + 1) D / 2) of
-// its row, in groups of 8 bytes = 8 consecutive channels.
-template <int D>
-__global__ __launch_bounds__(256) void quantize_k_kernel(const QuantLaunch a) {
-  constexpr int kGroups = D / 16;  // 8-byte output groups per lane
+// One wave per (batch, KV head, half-tile), 4 per workgroup.  Lane l owns
+// the 8-channel group m = l % (D / 8) of rows l / (D / 8) + (64 / (D / 8)) i:
+// each load instruction reads whole 2D-byte rows (coalesced), and the 8
+// channels of a group land on 8 consecutive bytes of the fp8 row (4 of the
+// fp4 row), so every lane stores its own codes.
+template <int D, bool kFp4>
+__global__ __launch_bounds__(256) void quantize_kernel(const QuantLaunch a) {
+  constexpr int kGroups = D / 8;                  // 8-channel groups per row
+  constexpr int kRowsPerStep = 64 / kGroups;      // rows one load instruction covers
+  constexpr int kSteps = kHalfKeys / kRowsPerStep;
+  constexpr float kMax = kFp4 ? 6.0f : 448.0f;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t blk = static_cast<int64_t>(blockIdx.x) * 4 + wave;
   if (blk >= a.n_blocks) return;
@@ -45,106 +50,55 @@ __global__ __launch_bounds__(256) void quantize_k_kernel(const QuantLaunch a) {
   const int hb = static_cast<int>(blk % nh);
   const int64_t bg = blk / nh;
   const int b = static_cast<int>(bg / a.heads_kv), g = static_cast<int>(bg % a.heads_kv);
-  const int key = hb * kHalfKeys + (lane >> 1);
-  const bool valid = key < a.seqlen;
-  const int p0 = (lane & 1) * (D / 2);
-  const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.k_stride[0] + g * a.k_stride[1] +
-                       static_cast<int64_t>(valid ? key : 0) * a.k_stride[2];
-  u32x4 in[kGroups];
+  const int m = lane % kGroups, r0 = lane / kGroups;
+  const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.k_stride[0] + g * a.k_stride[1] + 8 * m;
+  u32x4 in[kSteps];
   float amax = 0.0f;
 #pragma unroll
-  for (int gi = 0; gi < kGroups; ++gi) {
-    const int p = p0 + gi * 8;
-    const int s = p >> 6, h = (p >> 5) & 1, j = p & 31;
-    const int d0 = 64 * s + 16 * (j >> 3) + 8 * h;
+  for (int i = 0; i < kSteps; ++i) {
+    const int key = hb * kHalfKeys + r0 + kRowsPerStep * i;
     u32x4 w = {0u, 0u, 0u, 0u};
-    if (valid) w = *reinterpret_cast<const u32x4*>(kp + d0);
-    in[gi] = w;
+    if (key < a.seqlen) w = *reinterpret_cast<const u32x4*>(kp + static_cast<int64_t>(key) * a.k_stride[2]);
+    in[i] = w;
 #pragma unroll
     for (int x = 0; x < 4; ++x) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[x])), fabsf(bf16_hi(w[x]))));
   }
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
-  if (lane == 0) a.scale[blk] = amax / 448.0f;
-  if (!valid) return;
-  uint32_t* out = reinterpret_cast<uint32_t*>(static_cast<char*>(a.k8) + (bg * a.seqlen + key) * D + p0);
+  const float inv = amax > 0.0f ? kMax / amax : 0.0f;
+  if (lane == 0) a.scale[blk] = amax / kMax;
+  // channels 8 m .. 8 m + 7 = k-step s = m / 8, lane half h = m % 2, elements
+  // 8 ((m % 8) / 2) .. + 7 of that (step, half) in the operand order
+  const int s = m / 8, h = m % 2, e0 = 8 * ((m % 8) / 2);
+  const int out_off = kFp4 ? 16 * (2 * s + h) + e0 / 2 : 64 * s + 32 * h + e0;
+  constexpr int kOutRow = kFp4 ? D / 2 : D;
 #pragma unroll
-  for (int gi = 0; gi < kGroups; ++gi) {
-    uint32_t o2[2];
+  for (int i = 0; i < kSteps; ++i) {
+    const int key = hb * kHalfKeys + r0 + kRowsPerStep * i;
+    if (key >= a.seqlen) continue;
+    float v[8];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const uint32_t w0 = in[gi][2 * half], w1 = in[gi][2 * half + 1];
-      const float v0 = fminf(fmaxf(bf16_lo(w0) * inv, -448.0f), 448.0f);
-      const float v1 = fminf(fmaxf(bf16_hi(w0) * inv, -448.0f), 448.0f);
-      const float v2 = fminf(fmaxf(bf16_lo(w1) * inv, -448.0f), 448.0f);
-      const float v3 = fminf(fmaxf(bf16_hi(w1) * inv, -448.0f), 448.0f);
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
-      word = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, word, true);
-      o2[half] = static_cast<uint32_t>(word);
+    for (int x = 0; x < 4; ++x) {
+      v[2 * x] = fminf(fmaxf(bf16_lo(in[i][x]) * inv, -kMax), kMax);
+      v[2 * x + 1] = fminf(fmaxf(bf16_hi(in[i][x]) * inv, -kMax), kMax);
     }
-    out[2 * gi] = o2[0];
-    out[2 * gi + 1] = o2[1];
-  }
-}
-
-// fp4 copy: one wave per (batch, KV head, half-tile).  Lane l owns key l / 2
-// of the block and output bytes [(l % 2) D / 4, (l % 2 + 1) D / 4) of its
-// row: D / 64 blocks of 16 bytes, each from 4 groups of 8 channels.
-template <int D>
-__global__ __launch_bounds__(256) void quantize_k4_kernel(const QuantLaunch a) {
-  constexpr int kBlocks = D / 64;  // 16-byte output blocks per lane
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t blk = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-  if (blk >= a.n_blocks) return;
-  const int nh = (a.seqlen + kHalfKeys - 1) / kHalfKeys;
-  const int hb = static_cast<int>(blk % nh);
-  const int64_t bg = blk / nh;
-  const int b = static_cast<int>(bg / a.heads_kv), g = static_cast<int>(bg % a.heads_kv);
-  const int key = hb * kHalfKeys + (lane >> 1);
-  const bool valid = key < a.seqlen;
-  const int b0 = (lane & 1) * kBlocks;  // first output block of this lane
-  const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.k_stride[0] + g * a.k_stride[1] +
-                       static_cast<int64_t>(valid ? key : 0) * a.k_stride[2];
-  u32x4 in[kBlocks][4];
-  float amax = 0.0f;
-#pragma unroll
-  for (int bi = 0; bi < kBlocks; ++bi) {
-    const int blkid = b0 + bi, st = blkid >> 1, h = blkid & 1;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (valid) x = *reinterpret_cast<const u32x4*>(kp + 64 * st + 16 * w + 8 * h);
-      in[bi][w] = x;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(x[j])), fabsf(bf16_hi(x[j]))));
-    }
-  }
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  const float inv = amax > 0.0f ? 6.0f / amax : 0.0f;
-  if (lane == 0) a.scale[blk] = amax / 6.0f;
-  if (!valid) return;
-  u32x4* out = reinterpret_cast<u32x4*>(static_cast<char*>(a.k8) + (bg * a.seqlen + key) * (D / 2)) + b0;
-#pragma unroll
-  for (int bi = 0; bi < kBlocks; ++bi) {
-    u32x4 o;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      float v[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[2 * j] = fminf(fmaxf(bf16_lo(in[bi][w][j]) * inv, -6.0f), 6.0f);
-        v[2 * j + 1] = fminf(fmaxf(bf16_hi(in[bi][w][j]) * inv, -6.0f), 6.0f);
-      }
+    char* row = static_cast<char*>(a.k8) + (bg * a.seqlen + key) * kOutRow + out_off;
+    if constexpr (kFp4) {
       unsigned word = 0;
       word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[0], v[1], 1.0f, 0);
       word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[2], v[3], 1.0f, 1);
       word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[4], v[5], 1.0f, 2);
       word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, v[6], v[7], 1.0f, 3);
-      o[w] = word;
+      *reinterpret_cast<uint32_t*>(row) = word;
+    } else {
+      int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w0, true);
+      int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], w1, true);
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 o = {static_cast<uint32_t>(w0), static_cast<uint32_t>(w1)};
+      *reinterpret_cast<u32x2*>(row) = o;
     }
-    out[bi] = o;
   }
 }
 
@@ -153,19 +107,17 @@ __global__ __launch_bounds__(256) void quantize_k4_kernel(const QuantLaunch a) {
 int launch_quantize_k(const QuantLaunch& a, void* stream) {
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const unsigned grid = static_cast<unsigned>((a.n_blocks + 3) / 4);
+  if (a.head_dim != 128 && a.head_dim != 64) return fail(TRI_ERR_UNSUPPORTED, "head_dim %d", a.head_dim);
   if (a.fp4) {
     if (a.head_dim == 128)
-      hipLaunchKernelGGL(quantize_k4_kernel<128>, dim3(grid), dim3(256), 0, s, a);
-    else if (a.head_dim == 64)
-      hipLaunchKernelGGL(quantize_k4_kernel<64>, dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((quantize_kernel<128, true>), dim3(grid), dim3(256), 0, s, a);
     else
-      return fail(TRI_ERR_UNSUPPORTED, "head_dim %d", a.head_dim);
-  } else if (a.head_dim == 128)
-    hipLaunchKernelGGL(quantize_k_kernel<128>, dim3(grid), dim3(256), 0, s, a);
-  else if (a.head_dim == 64)
-    hipLaunchKernelGGL(quantize_k_kernel<64>, dim3(grid), dim3(256), 0, s, a);
-  else
-    return fail(TRI_ERR_UNSUPPORTED, "head_dim %d", a.head_dim);
+      hipLaunchKernelGGL((quantize_kernel<64, true>), dim3(grid), dim3(256), 0, s, a);
+  } else if (a.head_dim == 128) {
+    hipLaunchKernelGGL((quantize_kernel<128, false>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((quantize_kernel<64, false>), dim3(grid), dim3(256), 0, s, a);
+  }
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(TRI_ERR_HIP, "quantize launch failed: %s", hipGetErrorString(err));
   return TRI_OK;
