@@ -177,10 +177,25 @@ def measure_clock(fn, launch_ms, seconds=2.5, skip_s=1.0):
     return sum(samples) / len(samples), f"{len(samples)} samples over {n} launches (mean of the XCD clocks)"
 
 
-def cpu_baseline(bits, cfg, plan, n_random_tiles=128):
+def sample_tiles(N, n_random_tiles=128):
+    """Query tiles of the oracle sample: {0, 1, 15, 16, 17, nq-2, nq-1} plus
+    `n_random_tiles` seeded random middle tiles (15..17 straddle the 2048-key
+    window edge)."""
+    nq = -(-N // 128)
+    rng = np.random.default_rng(1)
+    middle = np.arange(18, max(18, nq - 2))
+    tiles = sorted({0, 1, 15, 16, 17, nq - 2, nq - 1} |
+                   set(int(x) for x in rng.choice(middle, min(n_random_tiles, middle.size),
+                                                   replace=False)))
+    tiles = [t for t in tiles if 0 <= t < nq]
+    rows = np.concatenate([np.arange(t * 128, min(N, (t + 1) * 128)) for t in tiles])
+    return tiles, rows
+
+
+def cpu_baseline(bits, cfg, plan):
     """The fp64 oracle, as it stands, on a bounded sample of the same layer:
-    query tiles {0, 1, 15, 16, 17, nq-2, nq-1} plus `n_random_tiles` seeded
-    random middle tiles, all heads (10-30 s of host work at 128K)."""
+    the rows of ``sample_tiles``, all heads (10-30 s of host work at 128K).
+    Returns (the cpu_baseline object, (rows, oracle O, oracle LSE))."""
     from oracle import attention as oatt
     import synth
     try:
@@ -190,20 +205,13 @@ def cpu_baseline(bits, cfg, plan, n_random_tiles=128):
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
     N, Hq, d = cfg["N"], cfg["Hq"], cfg["d"]
-    nq = -(-N // 128)
-    rng = np.random.default_rng(1)
-    middle = np.arange(18, max(18, nq - 2))
-    tiles = sorted({0, 1, 15, 16, 17, nq - 2, nq - 1} |
-                   set(int(x) for x in rng.choice(middle, min(n_random_tiles, middle.size),
-                                                   replace=False)))
-    tiles = [t for t in tiles if 0 <= t < nq]
-    rows = np.concatenate([np.arange(t * 128, min(N, (t + 1) * 128)) for t in tiles])
+    tiles, rows = sample_tiles(N)
     kept = sum(int(plan.row_ptr[t + 1] - plan.row_ptr[t]) for t in tiles)
     flops = 4.0 * 128 * 64 * d * kept * Hq * cfg["B"]
     f64 = synth.bf16_bits_to_f64
     q, k, v = f64(bits[0]), f64(bits[1]), f64(bits[2])
     t0 = time.perf_counter()
-    oatt.attention(q, k, v, "triangle", cfg["sink"], cfg["window"], cfg["last_q"], rows=rows)
+    ro, rl = oatt.attention(q, k, v, "triangle", cfg["sink"], cfg["window"], cfg["last_q"], rows=rows)
     dt = time.perf_counter() - t0
     total_flops = 4.0 * 128 * 64 * d * plan.k_tile.size * Hq * cfg["B"]
     cpu_model = ""
@@ -224,7 +232,25 @@ def cpu_baseline(bits, cfg, plan, n_random_tiles=128):
                    f"all {Hq} heads ({rows.size} rows, {kept} kept tiles/head): "
                    f"{dt:.2f} s; kept-tile FLOPs of the sample / time; full layer extrapolated "
                    f"{dt * total_flops / flops:.1f} s"),
-    }
+    }, (rows, ro, rl)
+
+
+def sample_of(o, lse, rows):
+    """Host copy of the sample rows of a layer's outputs (O as float64)."""
+    import torch
+    idx = torch.from_numpy(rows).to(o.device)
+    return (o[:, :, idx].float().cpu().numpy().astype(np.float64),
+            lse[:, :, idx].cpu().numpy().astype(np.float64))
+
+
+def error_vs_oracle(sample, ref):
+    """Max and mean |dO|, max |dLSE| / max(1, |LSE|) of a sample against the
+    oracle rows."""
+    o, l = sample
+    _, ro, rl = ref
+    err = np.abs(o - ro)
+    return {"o_max_abs_err": float(f"{err.max():.3e}"), "o_mean_abs_err": float(f"{err.mean():.3e}"),
+            "lse_max_rel_err": float(f"{(np.abs(l - rl) / np.maximum(1.0, np.abs(rl))).max():.3e}")}
 
 
 def bench_dynamic(t, args, dense_ms, d, Hq, B, dev, stream):
@@ -253,6 +279,7 @@ def bench_per_head(t, args, cfg, d, Hq, B, dev, stream):
     """The triangle layer with per-head boundaries (TriAttention page: each
     head's region as diagonal-distance boundaries): windows 512, 1024, 2048,
     4096 and sinks 0 / 128 cycling over the heads, last-Q as configured."""
+    import torch
     import static_triangle_sparse_amd as tsa
     window = [512 << (h % 4) for h in range(Hq)]
     sink = [128 * (h % 2) for h in range(Hq)]
@@ -273,7 +300,8 @@ def bench_per_head(t, args, cfg, d, Hq, B, dev, stream):
     plain = lambda: tsa.tri_attn_prefill(t, short.mp, short.d_row_ptr.data_ptr(), short.d_k_tile.data_ptr(),
                                          short.d_flags.data_ptr(), stream)
     chunk = 128
-    ws = tsa.split_workspace(tsa.tri_attn_split_workspace_size(t, short.mp, chunk), dev)
+    ws = tsa.split_workspace(tsa.tri_attn_split_workspace_size(t, short.mp, chunk), dev,
+                             torch.cuda.current_stream(dev))
     split = lambda: tsa.tri_attn_prefill_split(t, short.mp, None, None, short.d_row_ptr.data_ptr(),
                                                short.d_k_tile.data_ptr(), short.d_flags.data_ptr(), chunk,
                                                ws.data_ptr(), ws.numel(), stream)
@@ -288,47 +316,60 @@ def bench_per_head(t, args, cfg, d, Hq, B, dev, stream):
     return out
 
 
-def bench_tiered(t, args, cfg, plan, tri_ms, d, Hq, B, dev, stream):
+def bench_tiered(t, args, cfg, plan, tri_ms, d, Hq, B, dev, stream, rows):
     """The triangle layer with precision tiers (TriAttention page: per-head
-    diagonal-distance boundaries choose each tile's precision, 4-bit and 8-bit
-    tiers): key tiles at least --low-dist keys behind the query tile scored in
-    fp8 (e4m3), the rest in bf16; then two settings with the fp4 (e2m1) tier.
-    The fp8 and fp4 copies of K and the layer are timed separately."""
+    diagonal-distance boundaries choose each tile's precision, 8-bit near and
+    4-bit far): fp8 (e4m3) scores on key tiles at least --low-dist keys behind
+    the query tile, fp4 (e2m1) from --fp4-dist, bf16 on the rest; then two more
+    settings.  The fp8 and fp4 copies of K and the layers are timed
+    separately.  Each setting's sample rows are kept for its error against
+    the exact triangle layer (filled in once the oracle has run)."""
     import numpy as np
     import torch
     import static_triangle_sparse_amd as tsa
     qk = tsa.QuantizedK(t, dev, fp4=True)
     quant_ms, _ = time_launches(lambda: qk.run(t, stream), args.dense_steps, 1)
-    rows = np.repeat(np.arange(plan.row_ptr.size - 1), np.diff(plan.row_ptr))
-    dist_min = rows * 128 - (plan.k_tile.astype(np.int64) * 64 + 63)
+    rows_of = np.repeat(np.arange(plan.row_ptr.size - 1), np.diff(plan.row_ptr))
+    dist_min = rows_of * 128 - (plan.k_tile.astype(np.int64) * 64 + 63)
+    o = torch.empty((B, Hq, cfg["N"], d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Hq, cfg["N"]), dtype=torch.float32, device=dev)
+    tt = tsa.AttnTensors.from_buffer_copy(t)
+    tt.o, tt.lse = o.data_ptr(), lse.data_ptr()
+    tt.o_stride[:] = [o.stride(0), o.stride(1), o.stride(2)]
+    tt.lse_stride[:] = [lse.stride(0), lse.stride(1)]
+    tt.o_dtype = tsa.TRI_DTYPE_BF16
+    samples = []
 
     def layer(low_dist, fp4_dist=None):
         d8 = torch.from_numpy(np.full(Hq, low_dist, np.int32)).to(dev)
         d4 = None if fp4_dist is None else torch.from_numpy(np.full(Hq, fp4_dist, np.int32)).to(dev)
         f4 = (None, None, None) if d4 is None else (d4.data_ptr(), qk.k4.data_ptr(), qk.scale4.data_ptr())
-        run = lambda: tsa.tri_attn_prefill_tiered(t, plan.mp, d8.data_ptr(), qk.k8.data_ptr(), qk.scale.data_ptr(),
+        run = lambda: tsa.tri_attn_prefill_tiered(tt, plan.mp, d8.data_ptr(), qk.k8.data_ptr(), qk.scale.data_ptr(),
                                                   *f4, plan.d_row_ptr.data_ptr(), plan.d_k_tile.data_ptr(),
                                                   plan.d_flags.data_ptr(), stream)
         ms, _ = time_launches(run, args.steps, args.warmup)
+        torch.cuda.synchronize()
         n4 = int(np.sum(dist_min >= fp4_dist)) if fp4_dist is not None else 0
         n8 = int(np.sum(dist_min >= low_dist)) - (int(np.sum((dist_min >= low_dist) & (dist_min >= fp4_dist)))
                                                   if fp4_dist is not None else 0)
-        return {"fp8_from": low_dist, "fp4_from": fp4_dist, "ms": round(ms, 4),
-                "fp8_tile_fraction": round(n8 / max(1, plan.k_tile.size), 4),
-                "fp4_tile_fraction": round(n4 / max(1, plan.k_tile.size), 4),
-                "speedup_vs_bf16_triangle": round(tri_ms / ms, 3)}
+        out = {"fp8_from": low_dist, "fp4_from": fp4_dist, "ms": round(ms, 4),
+               "fp8_tile_fraction": round(n8 / max(1, plan.k_tile.size), 4),
+               "fp4_tile_fraction": round(n4 / max(1, plan.k_tile.size), 4),
+               "speedup_vs_bf16_triangle": round(tri_ms / ms, 3)}
+        if rows is not None:
+            samples.append((out, sample_of(o, lse, rows)))
+        return out
     flops = 4.0 * 128 * 64 * d * plan.k_tile.size * Hq * B
-    main_ = layer(args.low_dist)
-    main_["kept_tflops"] = round(flops / (main_["ms"] * 1e-3) / 1e12, 2)
-    three = [layer(0, 1024), layer(10 ** 6, 0)]
-    print(f"[bench] tiered triangle (fp8 scores from distance {args.low_dist}): K to fp8 + fp4 "
+    main_ = layer(args.low_dist, args.fp4_dist if args.fp4_dist >= 0 else None)
+    main_["kept_tflops_bf16_equivalent"] = round(flops / (main_["ms"] * 1e-3) / 1e12, 2)
+    others = [layer(1024), layer(10 ** 6, 0)]
+    print(f"[bench] tiered triangle (fp8 from {main_['fp8_from']}, fp4 from {main_['fp4_from']}): K to fp8 + fp4 "
           f"{quant_ms:.3f} ms, layer {main_['ms']:.3f} ms ({main_['speedup_vs_bf16_triangle']}x); "
-          f"fp8 near / fp4 from 1024: {three[0]['ms']:.3f} ms; fp4 off the diagonal band: {three[1]['ms']:.3f} ms",
+          f"fp8 from 1024 only: {others[0]['ms']:.3f} ms; fp4 off the diagonal band: {others[1]['ms']:.3f} ms",
           file=sys.stderr, flush=True)
-    return {"low_dist": args.low_dist, "low_tile_fraction": main_["fp8_tile_fraction"],
-            "quantize_fp8_fp4_ms": round(quant_ms, 4), "attention_ms": main_["ms"],
-            "kept_tflops": main_["kept_tflops"], "speedup_vs_bf16_triangle": main_["speedup_vs_bf16_triangle"],
-            "with_fp4_tier": three}
+    return {"setting": main_, "other_settings": others, "quantize_fp8_fp4_ms": round(quant_ms, 4),
+            "note": ("kept_tflops_bf16_equivalent counts fp8/fp4 tiles as bf16 work (4*128*64*d FLOPs); "
+                     "errors are against the exact (fp64) triangle layer on the oracle sample rows")}, samples
 
 
 def main(argv=None):
@@ -343,9 +384,12 @@ def main(argv=None):
                     help="also time the triangle layer with per-head windows (0: skip)")
     ap.add_argument("--dyn-alpha", type=float, default=0.9,
                     help="keep threshold of the dynamic block-sparse dense layer (0 disables it)")
-    ap.add_argument("--low-dist", type=int, default=1024,
+    ap.add_argument("--low-dist", type=int, default=0,
                     help="precision tiers: fp8 scores on key tiles at least this many keys behind "
-                         "the query tile (negative: disable the tiered layer)")
+                         "the query tile (negative: disable the tiered layers)")
+    ap.add_argument("--fp4-dist", type=int, default=1024,
+                    help="precision tiers: fp4 scores from this distance on (negative: no fp4 tier); "
+                         "the default pair is the page's 8-bit-near, 4-bit-far scheme")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the 2.5 s shader-clock run (profiling runs)")
@@ -374,6 +418,15 @@ def main(argv=None):
     B, Hq, N, d = cfg["B"], cfg["Hq"], cfg["N"], cfg["d"]
     o = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    # the host planner (sizing call + fill call), outside the timed region
+    mp = tsa.mask_params(N, "triangle", cfg["sink"], cfg["window"], cfg["last_q"])
+    tsa.tri_attn_plan(mp)
+    t0 = time.perf_counter()
+    plan_runs = 20
+    for _ in range(plan_runs):
+        tsa.tri_attn_plan(mp)
+    plan_ms = (time.perf_counter() - t0) * 1e3 / plan_runs
+    print(f"[bench] host planner: {plan_ms:.3f} ms", file=sys.stderr, flush=True)
     plan = tsa.device_plan(N, "triangle", cfg["sink"], cfg["window"], cfg["last_q"], dev)
     t = tsa.make_tensors(q, k, v, o, lse)
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -391,6 +444,10 @@ def main(argv=None):
     runs["cold"]["flush"] = "512 MiB device write before each launch, outside the events"
     print(f"[bench] triangle per launch: warm median {runs['warm']['median_ms']:.3f} ms, cold median "
           f"{runs['cold']['median_ms']:.3f} ms", file=sys.stderr, flush=True)
+    # the sample rows of the oracle baseline, kept for the error figures
+    rows = None if args.no_cpu_baseline else sample_tiles(N)[1]
+    torch.cuda.synchronize()
+    tri_sample = sample_of(o, lse, rows) if rows is not None else None
     # the same launches for ~2.5 s more, with the shader clock read meanwhile:
     # the fraction of the MFMA peak at the clock the chip actually ran
     sclk, detail = (None, "skipped (--no-clock)") if args.no_clock else measure_clock(tri, tri_ms)
@@ -415,8 +472,10 @@ def main(argv=None):
             extra["dynamic_dense"] = bench_dynamic(t, args, dense_ms, d, Hq, B, dev, stream)
     if args.per_head:
         extra["per_head_triangle"] = bench_per_head(t, args, cfg, d, Hq, B, dev, stream)
+    tier_samples = []
     if args.low_dist >= 0:
-        extra["tiered_triangle"] = bench_tiered(t, args, cfg, plan, tri_ms, d, Hq, B, dev, stream)
+        extra["tiered_triangle"], tier_samples = bench_tiered(t, args, cfg, plan, tri_ms, d, Hq, B, dev,
+                                                              stream, rows)
 
     if args.calib_copy_mib:
         nbytes = args.calib_copy_mib << 20
@@ -431,7 +490,12 @@ def main(argv=None):
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample) ...", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(bits, cfg, plan)
+        cpu, ref = cpu_baseline(bits, cfg, plan)
+        # the timed bf16 layer and each precision-tier setting against the exact
+        # (fp64) triangle layer on the same rows
+        extra["triangle_error_vs_oracle"] = error_vs_oracle(tri_sample, ref)
+        for entry, sample in tier_samples:
+            entry["error_vs_exact_triangle"] = error_vs_oracle(sample, ref)
 
     traffic = read_traffic(args.config)
     out = {
@@ -453,6 +517,8 @@ def main(argv=None):
                    "window": cfg["window"], "last_q": cfg["last_q"], "tile": "128x64",
                    "o_dtype": "bf16", "kept_tiles_per_head": tiles},
         "triangle_ms": round(tri_ms, 4),
+        "plan_ms": round(plan_ms, 4),
+        "plan_note": "host planner, one tri_attn_plan sizing call plus one fill call, once per shape",
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "triangle_per_launch": runs,
         "measured_clock": at_clock,
@@ -478,22 +544,18 @@ def bench_stack(args, cfg, dev):
         layers.append((q, k, v))
     o = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
-    plan = tsa.device_plan(N, "triangle", cfg["sink"], cfg["window"], cfg["last_q"], dev)
-    stream = torch.cuda.current_stream(dev).cuda_stream
+    stream = torch.cuda.current_stream(dev)
     descs = [tsa.make_tensors(q, k, v, o, lse) for (q, k, v) in layers]
+    tsa.device_plan(N, "triangle", cfg["sink"], cfg["window"], cfg["last_q"], torch.cuda.current_device())
     modes = [tsa.layer_mode(l, cfg["tri_start"]) for l in range(L)]
 
     def step():
-        for t, m in zip(descs, modes):
-            if m == "causal":
-                tsa.dense_causal_prefill(t, stream)
-            else:
-                tsa.tri_attn_prefill(t, plan.mp, plan.d_row_ptr.data_ptr(), plan.d_k_tile.data_ptr(),
-                                     plan.d_flags.data_ptr(), stream)
+        tsa.stack_prefill(descs, cfg["tri_start"], cfg["sink"], cfg["window"], cfg["last_q"], stream)
 
     steps = max(1, min(args.steps, 3))
     ms, _ = time_launches(step, steps, min(args.warmup, 1))
-    tiles = kept_tiles_per_head(plan)
+    tiles = kept_tiles_per_head(tsa.device_plan(N, "triangle", cfg["sink"], cfg["window"], cfg["last_q"],
+                                                torch.cuda.current_device()))
     ctiles = causal_tiles_per_head(N)
     n_dense = sum(m == "causal" for m in modes)
     flops = 4.0 * 128 * 64 * d * Hq * B * (n_dense * ctiles + (L - n_dense) * tiles)

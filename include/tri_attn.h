@@ -91,6 +91,27 @@ int tri_attn_plan(const tri_mask_params* mp, int32_t* row_ptr, int32_t* k_tile,
                   uint8_t* flags, int64_t capacity, int32_t* n_qtiles_out,
                   int64_t* nnz_out);
 
+/*
+ * tri_attn_check_plan -- host only: checks a host copy of a tile plan before
+ * its device copy is handed to a prefill call (the kernel walks the arrays
+ * as given).  The plan is CSR over n_rows list rows (a multiple of n_qtiles);
+ * row r lists key tiles of query tile r % n_qtiles.  With heads > 0, row r
+ * follows head (r / n_qtiles) % heads's sink[] and window[] (the layout of
+ * tri_attn_plan_heads); with heads = 0 (sink, window may be NULL) every row
+ * follows *mp.  Checked: row_ptr[0] = 0, row_ptr non-decreasing up to
+ * row_ptr[n_rows] = nnz; within a row, key tiles strictly ascending and
+ * inside the row's causal range; each listed tile holds a kept pair of the
+ * mask (TriangleMix blog "介绍"; 36kr interview, technical motivation); its
+ * flag equals the tile_flag definition of tri_attn_plan.  A list of some of
+ * the kept tiles passes (a dynamic selection under kind = TRI_MASK_CAUSAL).
+ * Returns TRI_OK, or TRI_ERR_INVALID with the first bad entry named in
+ * tri_attn_last_error().  Reads row_ptr[0 .. n_rows], k_tile[0 .. nnz),
+ * flags[0 .. nnz); writes nothing.
+ */
+int tri_attn_check_plan(const tri_mask_params* mp, int32_t heads, const int64_t* sink,
+                        const int64_t* window, const int32_t* row_ptr, int64_t n_rows,
+                        const int32_t* k_tile, const uint8_t* flags, int64_t nnz);
+
 /* Device tensors of one layer.  Strides are in elements, for the (batch, head,
  * token) axes; the channel axis is contiguous.  q, k, v are bf16, 16-byte
  * aligned, with token strides that are multiples of 8 elements; the N token
@@ -242,29 +263,31 @@ int tri_attn_prefill_heads(const tri_attn_tensors* t, const tri_mask_params* mp,
  * low_dist[h] (every query-key distance in the tile reaches the boundary).
  * A LOW tile's score is softmax_scale * s_q * s_k * <q8, k8>, with
  *   s_q = amax |q row| / 448,           q8 = e4m3(q * (448 / amax_q)),
- *   s_k = amax |K of the 32-key half| / 448, k8 = e4m3(k * (448 / amax_k)),
+ *   s_k = amax |K of the key tile| / 448, k8 = e4m3(k * (448 / amax_k)),
  * rounded to nearest even after clamping to +-448 (all-zero blocks: scale 0).
+ * The page assigns a precision per query-key tile, so one K scale covers the
+ * TRI_KERNEL_BLOCK_K keys of a key tile.
  *
  * tri_attn_quantize_k_sizes -- bytes of the fp8 K (batch*heads_kv*N*head_dim)
- * and number of scales (batch*heads_kv*ceil(N/32)).
+ * and number of scales (batch*heads_kv*ceil(N/64)).
  * tri_attn_quantize_k -- enqueue the fp8 copy of t->k: d_k8 (16-byte
  * aligned) holds, for each (batch, KV head), N rows of head_dim bytes in the
  * kernel's operand order (byte 64s + 32h + j of a row is channel
- * 64s + 16(j/8) + 8h + j%8); d_scale [batch, heads_kv, ceil(N/32)] f32.
+ * 64s + 16(j/8) + 8h + j%8); d_scale [batch, heads_kv, ceil(N/64)] f32.
  *
  * The page's two lower tiers are 4-bit and 8-bit: a second per-head boundary
  * selects fp4 (e2m1, on the same matrix cores at twice the fp8 rate) for
  * the farthest tiles.  The farthest tier wins: a tile is fp4 when
  * 128*t - (64*kt + 63) >= fp4_dist[h], else fp8 when >= low_dist[h], else
- * bf16.  fp4 scores use s_q = amax |q row| / 6, s_k = amax / 6 of the 32-key
- * half, codes e2m1(clamp(x * 6 / amax, -6, 6)) rounded to nearest, ties to
+ * bf16.  fp4 scores use s_q = amax |q row| / 6, s_k = amax / 6 of the key
+ * tile, codes e2m1(clamp(x * 6 / amax, -6, 6)) rounded to nearest, ties to
  * the even code.
  *
  * tri_attn_quantize_k4_sizes / tri_attn_quantize_k4 -- the fp4 copy of t->k:
  * d_k4 (16-byte aligned) holds, per (batch, KV head), N rows of head_dim / 2
  * bytes; 16-byte block 2s + h of a row holds the 32 elements e of k-step s,
  * lane half h (channel 64s + 16(e/8) + 8h + e%8, as in the fp8 copy) at
- * nibble e of the block; d_scale [batch, heads_kv, ceil(N/32)] f32.
+ * nibble e of the block; d_scale [batch, heads_kv, ceil(N/64)] f32.
  * tri_attn_prefill_tiered -- tri_attn_prefill with the LOW tiles scored from
  * d_k8 / d_scale (the output of tri_attn_quantize_k for the same K) and the
  * device int32 boundaries d_head_low_dist [heads_q], and, when

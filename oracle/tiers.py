@@ -14,17 +14,18 @@ skipping is the triangle plan itself, so one per-head boundary remains:
   is computed in bf16 as in the plain triangle layer;
 * on LOW tiles the score is scale * s_q * s_k * <q8, k8>, with
     - s_q = amax(|q row|) / 448 and q8 = e4m3(q * (448 / amax)),
-    - s_k = amax(|K of the 32-key half-tile|) / 448 and
-      k8 = e4m3(k * (448 / amax)),
+    - s_k = amax(|K of the key tile|) / 448 and k8 = e4m3(k * (448 / amax)):
+      the page assigns a precision to each query-key tile, so the key tile
+      (the grid's Bk keys) is the block that shares one scale,
   every scale and product formed in float32 as the GPU forms them (the
   rounding of a value to a code is an integer decision: both sides take it
-  in the same precision); an all-zero row or half-tile has scale 0;
+  in the same precision); an all-zero row or key tile has scale 0;
 * values are then combined in one softmax over the row's kept keys.
 
 The page's tiers are 4-bit and 8-bit; a second per-head boundary dist4 adds
 the 4-bit one: a kept tile whose smallest distance is >= dist4[h] is scored
 in fp4 (e2m1: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), with s_q = amax / 6,
-s_k = amax of the 32-key half-tile / 6 and codes e2m1(clamp(x * 6 / amax)),
+s_k = amax of the key tile / 6 and codes e2m1(clamp(x * 6 / amax)),
 rounded to nearest, ties to the even code, in float32 as on the GPU.  The
 farthest tier wins: fp4 if d >= dist4, else fp8 if d >= dist, else bf16.
 
@@ -153,17 +154,16 @@ def attention(q, k, v, sink, window, last_q, dist, scale=None, rows=None, block_
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     rows = np.arange(N) if rows is None else np.asarray(rows, np.int64)
-    half = block_k // 2
-    nh = -(-N // half)
-    # fp8 keys per 32-key half-tile (keys >= N are zero, as the GPU loads them)
-    kp = np.zeros((B, Hkv, nh * half, d))
+    nk = -(-N // block_k)
+    # quantized keys per key tile (keys >= N are zero, as the GPU loads them)
+    kp = np.zeros((B, Hkv, nk * block_k, d))
     kp[:, :, :N] = k
-    kq, ks = quantize(kp.reshape(B, Hkv, nh, half * d), axis=3)
-    k8 = kq.reshape(B, Hkv, nh * half, d)[:, :, :N]
-    s_k = np.repeat(ks[..., 0], half, axis=2)[:, :, :N]               # [B, Hkv, N]
-    kq4, ks4 = quantize4(kp.reshape(B, Hkv, nh, half * d), axis=3)
-    k4 = kq4.reshape(B, Hkv, nh * half, d)[:, :, :N]
-    s_k4 = np.repeat(ks4[..., 0], half, axis=2)[:, :, :N]
+    kq, ks = quantize(kp.reshape(B, Hkv, nk, block_k * d), axis=3)
+    k8 = kq.reshape(B, Hkv, nk * block_k, d)[:, :, :N]
+    s_k = np.repeat(ks[..., 0], block_k, axis=2)[:, :, :N]            # [B, Hkv, N]
+    kq4, ks4 = quantize4(kp.reshape(B, Hkv, nk, block_k * d), axis=3)
+    k4 = kq4.reshape(B, Hkv, nk * block_k, d)[:, :, :N]
+    s_k4 = np.repeat(ks4[..., 0], block_k, axis=2)[:, :, :N]
     o = np.zeros((B, Hq, rows.size, d))
     lse = np.zeros((B, Hq, rows.size))
     for b in range(B):

@@ -15,6 +15,7 @@ natural-log LSE [B, Hq, N] (f32).
 from __future__ import annotations
 
 import math
+import os
 
 import numpy as np
 
@@ -28,6 +29,7 @@ from ._abi import (  # noqa: F401
     tri_attn_quantize_k, tri_attn_quantize_k_sizes, tri_attn_work_item, tri_dyn_plan,
     tri_dyn_plan_sizes, tri_attn_prefill_split, tri_attn_split_work_item,
     tri_attn_split_workspace_size, tri_attn_quantize_k4, tri_attn_quantize_k4_sizes,
+    tri_attn_check_plan,
 )
 
 __all__ = [
@@ -37,23 +39,35 @@ __all__ = [
     "HeadPlan", "head_plan", "tri_attn_plan_heads", "tri_attn_prefill_heads",
     "QuantizedK", "quantize_k", "tri_attn_quantize_k", "tri_attn_prefill_tiered",
     "split_workspace", "tri_attn_prefill_split", "tri_attn_split_workspace_size",
+    "tri_attn_check_plan", "stack_prefill",
 ]
 
 _WORKSPACE = {}
 
 
-def split_workspace(nbytes: int, device):
-    """A device workspace of at least ``nbytes`` for split launches, kept for
-    the life of the process (one per device, grown on demand), so that it
-    outlives every launch enqueued with it."""
+def split_workspace(nbytes: int, device, stream=None):
+    """A device workspace of at least ``nbytes`` for split launches on
+    ``stream`` (a torch stream; default: the device's current stream), kept
+    for the life of the process and grown on demand, so that it outlives
+    every launch enqueued with it.  One per (device, stream): launches on one
+    stream are ordered, while launches on two streams sharing one workspace
+    would overwrite each other's partials."""
     import torch
-    key = str(device)
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    key = (str(device), int(stream.cuda_stream))
     ws = _WORKSPACE.get(key)
     if ws is None or ws.numel() < nbytes:
         # torch's caching allocator returns 512-byte-aligned blocks
         ws = torch.empty(max(256, nbytes), dtype=torch.uint8, device=device)
         _WORKSPACE[key] = ws
     return ws
+
+
+def _check_plans() -> bool:
+    """TRI_ATTN_CHECK_PLANS=1: every host plan built here is checked with
+    tri_attn_check_plan before its device copy is made."""
+    return os.environ.get("TRI_ATTN_CHECK_PLANS", "0") not in ("", "0")
 
 
 def layer_mode(layer: int, tri_start: int) -> str:
@@ -70,6 +84,8 @@ class DevicePlan:
         import torch
         self.mp = mp
         self.row_ptr, self.k_tile, self.flags = tri_attn_plan(mp)
+        if _check_plans():
+            tri_attn_check_plan(mp, self.row_ptr, self.k_tile, self.flags)
         self.d_row_ptr = torch.from_numpy(self.row_ptr).to(device)
         # never hand the kernel an empty allocation
         n = max(1, self.k_tile.size)
@@ -134,6 +150,10 @@ class HeadPlan:
         self.sink = np.asarray(sink, dtype=np.int64)
         self.window = np.asarray(window, dtype=np.int64)
         self.row_ptr, self.k_tile, self.flags = tri_attn_plan_heads(self.mp, self.sink, self.window)
+        if _check_plans():
+            tri_attn_check_plan(self.mp, self.row_ptr, self.k_tile, self.flags, self.sink, self.window)
+        self.heads = int(self.sink.size)
+        self.seqlen = int(seqlen)
         self.d_row_ptr = torch.from_numpy(self.row_ptr).to(device)
         n = max(1, self.k_tile.size)
         self.d_k_tile = torch.zeros(n, dtype=torch.int32, device=device)
@@ -157,6 +177,8 @@ class QuantizedK:
 
     def __init__(self, t: AttnTensors, device, fp4: bool = False):
         import torch
+        # the K it was made for: (batch, heads_kv, seqlen, head_dim)
+        self.shape = (int(t.batch), int(t.heads_kv), int(t.seqlen), int(t.head_dim))
         nbytes, nscales = tri_attn_quantize_k_sizes(t)
         self.k8 = torch.empty(max(16, nbytes), dtype=torch.uint8, device=device)
         self.scale = torch.empty(max(1, nscales), dtype=torch.float32, device=device)
@@ -167,6 +189,9 @@ class QuantizedK:
             self.scale4 = torch.empty(max(1, nscales4), dtype=torch.float32, device=device)
 
     def run(self, t: AttnTensors, stream: int) -> None:
+        if (t.batch, t.heads_kv, t.seqlen, t.head_dim) != self.shape:
+            raise ValueError(f"QuantizedK sized for K {self.shape}, called on "
+                             f"{(t.batch, t.heads_kv, t.seqlen, t.head_dim)}")
         tri_attn_quantize_k(t, self.k8.data_ptr(), self.scale.data_ptr(), stream)
         if self.k4 is not None:
             tri_attn_quantize_k4(t, self.k4.data_ptr(), self.scale4.data_ptr(), stream)
@@ -191,6 +216,8 @@ class DynPlan:
     def __init__(self, t: AttnTensors, device):
         import torch
         self.workspace_bytes, self.n_rows, self.max_nnz = tri_dyn_plan_sizes(t)
+        # the layer it lists: (batch, heads_q, seqlen)
+        self.shape = (int(t.batch), int(t.heads_q), int(t.seqlen))
         # torch's caching allocator returns 512-byte-aligned blocks
         self.workspace = torch.empty(max(256, self.workspace_bytes), dtype=torch.uint8, device=device)
         self.d_row_ptr = torch.empty(self.n_rows + 1, dtype=torch.int32, device=device)
@@ -198,6 +225,9 @@ class DynPlan:
         self.d_flags = torch.empty(max(1, self.max_nnz), dtype=torch.uint8, device=device)
 
     def run(self, t: AttnTensors, alpha: float, stream: int) -> None:
+        if (t.batch, t.heads_q, t.seqlen) != self.shape:
+            raise ValueError(f"DynPlan sized for (B, Hq, N) = {self.shape}, called on "
+                             f"{(t.batch, t.heads_q, t.seqlen)}")
         tri_dyn_plan(t, alpha, self.workspace.data_ptr(), self.workspace.numel(),
                      self.d_row_ptr.data_ptr(), self.d_k_tile.data_ptr(), self.d_flags.data_ptr(),
                      self.d_k_tile.numel(), stream)
@@ -215,12 +245,30 @@ def dyn_plan(q, k, alpha, scale=None, stream=None) -> DynPlan:
     return p
 
 
+def _per_head(x, Hq: int, name: str) -> np.ndarray:
+    """One int32 value per query head (clipped to the int32 range); anything
+    else is rejected, since the kernel reads entry h for every query head h."""
+    a = np.asarray(x, np.int64)
+    if a.ndim != 1 or a.size != Hq:
+        raise ValueError(f"{name} must hold one value per query head ({Hq}), got shape {a.shape}")
+    return np.clip(a, np.iinfo(np.int32).min, np.iinfo(np.int32).max).astype(np.int32)
+
+
+def _check_head_plan(plan, Hq: int, N: int) -> None:
+    if not isinstance(plan, HeadPlan):
+        raise ValueError("mode 'triangle_heads' needs plan= (a HeadPlan)")
+    if plan.heads != Hq or plan.seqlen != N:
+        raise ValueError(f"HeadPlan made for {plan.heads} heads and N = {plan.seqlen}, "
+                         f"the layer has {Hq} heads and N = {N}")
+
+
 def prefill(q, k, v, mode="triangle", sink=0, window=1, last_q=0, o_dtype=None, scale=None,
             out=None, lse=None, stream=None, plan=None, low_dist=None, split=None, fp4_dist=None):
     """One attention layer on the GPU; returns (o, lse).  ``mode`` is
     "triangle" (planned tile list), "triangle_heads" (a HeadPlan), "tiered"
-    (fp8 far tiles), "causal" (dense layer) or "lists" (per-head tile lists
-    of a DynPlan, causal mask inside the tiles).  ``split``: for "triangle" and
+    (fp8 far tiles; ``low_dist`` and ``fp4_dist`` hold one boundary per query
+    head), "causal" (dense layer) or "lists" (per-head tile lists of a
+    DynPlan, causal mask inside the tiles).  ``split``: for "triangle" and
     "triangle_heads", walk the last-Q rows in chunks of this many key tiles on
     separate workgroups (tri_attn_prefill_split)."""
     import torch
@@ -232,7 +280,8 @@ def prefill(q, k, v, mode="triangle", sink=0, window=1, last_q=0, o_dtype=None, 
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     t = make_tensors(q, k, v, out, lse, scale)
-    s = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
+    torch_stream = stream if stream is not None else torch.cuda.current_stream(q.device)
+    s = torch_stream.cuda_stream
     if split is not None and mode not in ("triangle", "triangle_heads"):
         raise ValueError("split= applies to modes 'triangle' and 'triangle_heads'")
     if split is not None:
@@ -240,12 +289,11 @@ def prefill(q, k, v, mode="triangle", sink=0, window=1, last_q=0, o_dtype=None, 
             p = device_plan(N, "triangle", sink, window, last_q, q.device)
             heads = (None, None)
         else:
-            if plan is None:
-                raise ValueError("mode 'triangle_heads' needs plan= (a HeadPlan)")
+            _check_head_plan(plan, Hq, N)
             p = plan
             heads = (plan.d_sink.data_ptr(), plan.d_window.data_ptr())
         nbytes = tri_attn_split_workspace_size(t, p.mp, int(split))
-        ws = split_workspace(nbytes, q.device)
+        ws = split_workspace(nbytes, q.device, torch_stream)
         tri_attn_prefill_split(t, p.mp, heads[0], heads[1], p.d_row_ptr.data_ptr(),
                                p.d_k_tile.data_ptr(), p.d_flags.data_ptr(), int(split), ws.data_ptr(),
                                ws.numel(), s)
@@ -256,36 +304,62 @@ def prefill(q, k, v, mode="triangle", sink=0, window=1, last_q=0, o_dtype=None, 
         tri_attn_prefill(t, p.mp, p.d_row_ptr.data_ptr(), p.d_k_tile.data_ptr(),
                          p.d_flags.data_ptr(), s)
     elif mode == "triangle_heads":
-        if plan is None:
-            raise ValueError("mode 'triangle_heads' needs plan= (a HeadPlan)")
+        _check_head_plan(plan, Hq, N)
         tri_attn_prefill_heads(t, plan.mp, plan.d_sink.data_ptr(), plan.d_window.data_ptr(),
                                plan.d_row_ptr.data_ptr(), plan.d_k_tile.data_ptr(),
                                plan.d_flags.data_ptr(), s)
     elif mode == "tiered":
-        if plan is None or low_dist is None:
+        if not isinstance(plan, QuantizedK) or low_dist is None:
             raise ValueError("mode 'tiered' needs plan= (a QuantizedK of k) and low_dist=")
-        import torch
+        kshape = (B, k.shape[1], N, d)
+        if plan.shape != kshape:
+            raise ValueError(f"QuantizedK made for K {plan.shape}, this layer's K is {kshape}")
         p = device_plan(N, "triangle", sink, window, last_q, q.device)
         # the device copy of the boundaries lives on the QuantizedK object, so it
         # outlives the enqueued kernel
-        clip = lambda x: torch.as_tensor(
-            np.clip(np.asarray(x, np.int64), np.iinfo(np.int32).min, np.iinfo(np.int32).max),
-            dtype=torch.int32).to(q.device)
-        plan.low_dist = clip(low_dist)
+        plan.low_dist = torch.from_numpy(_per_head(low_dist, Hq, "low_dist")).to(q.device)
         fp4_args = (None, None, None)
         if fp4_dist is not None:
             if plan.k4 is None:
                 raise ValueError("fp4_dist= needs a QuantizedK made with fp4=True")
-            plan.fp4_dist = clip(fp4_dist)
+            plan.fp4_dist = torch.from_numpy(_per_head(fp4_dist, Hq, "fp4_dist")).to(q.device)
             fp4_args = (plan.fp4_dist.data_ptr(), plan.k4.data_ptr(), plan.scale4.data_ptr())
         tri_attn_prefill_tiered(t, p.mp, plan.low_dist.data_ptr(), plan.k8.data_ptr(),
                                 plan.scale.data_ptr(), *fp4_args, p.d_row_ptr.data_ptr(),
                                 p.d_k_tile.data_ptr(), p.d_flags.data_ptr(), s)
     elif mode == "lists":
-        if plan is None:
+        if not isinstance(plan, DynPlan):
             raise ValueError("mode 'lists' needs plan= (a DynPlan)")
+        if plan.shape != (B, Hq, N):
+            raise ValueError(f"DynPlan made for (B, Hq, N) = {plan.shape}, the layer is {(B, Hq, N)}")
         tri_attn_prefill_lists(t, plan.d_row_ptr.data_ptr(), plan.d_k_tile.data_ptr(),
                                plan.d_flags.data_ptr(), s)
     else:
         raise ValueError(f"unknown mode {mode!r}")
     return out, lse
+
+
+def stack_prefill(layers, tri_start, sink, window, last_q, stream=None):
+    """Attention of a TriangleMix layer stack, enqueued layer after layer on
+    one stream: layer l runs dense causal if l < tri_start, else the triangle
+    pattern with (sink, window, last_q) (``layer_mode``).  ``layers`` is a
+    sequence of AttnTensors descriptors (make_tensors) of equal seqlen;
+    returns the mode each layer ran in."""
+    import torch
+    if not layers:
+        return []
+    N = int(layers[0].seqlen)
+    if any(int(t.seqlen) != N for t in layers):
+        raise ValueError("every layer of a stack has the same sequence length")
+    s = (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+    p = None
+    modes = [layer_mode(l, tri_start) for l in range(len(layers))]
+    for t, m in zip(layers, modes):
+        if m == "causal":
+            dense_causal_prefill(t, s)
+        else:
+            if p is None:
+                p = device_plan(N, "triangle", sink, window, last_q, torch.cuda.current_device())
+            tri_attn_prefill(t, p.mp, p.d_row_ptr.data_ptr(), p.d_k_tile.data_ptr(),
+                             p.d_flags.data_ptr(), s)
+    return modes

@@ -12,7 +12,9 @@ import os
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libtriattn.so")
+# TRI_ATTN_LIB names another build of the same library; only the host-only
+# sanitizer build of the test suite sets it
+LIB_PATH = os.environ.get("TRI_ATTN_LIB") or os.path.join(_PKG, "libtriattn.so")
 
 TRI_OK = 0
 TRI_ERR_INVALID = -1
@@ -102,6 +104,10 @@ def load() -> ctypes.CDLL:
                                   P(ctypes.c_uint8), ctypes.c_int64, P(ctypes.c_int32),
                                   P(ctypes.c_int64)]
     lib.tri_attn_plan.restype = ctypes.c_int
+    lib.tri_attn_check_plan.argtypes = [P(MaskParams), ctypes.c_int32, P(ctypes.c_int64),
+                                        P(ctypes.c_int64), P(ctypes.c_int32), ctypes.c_int64,
+                                        P(ctypes.c_int32), P(ctypes.c_uint8), ctypes.c_int64]
+    lib.tri_attn_check_plan.restype = ctypes.c_int
     lib.tri_attn_prefill.argtypes = [P(AttnTensors), P(MaskParams), ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.tri_attn_prefill.restype = ctypes.c_int
@@ -201,6 +207,29 @@ def tri_attn_plan(mp: MaskParams):
         flags.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), nnz.value, ctypes.byref(nq),
         ctypes.byref(nnz)))
     return row_ptr, k_tile[:nnz.value], flags[:nnz.value]
+
+
+def tri_attn_check_plan(mp: MaskParams, row_ptr, k_tile, flags, sink=None, window=None) -> None:
+    """Host check of a plan (tri_attn_check_plan); raises TriAttnError when
+    the arrays are not a valid plan for ``mp`` (per-head ``sink``/``window``:
+    the layout of tri_attn_plan_heads)."""
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    k_tile = np.ascontiguousarray(k_tile, dtype=np.int32)
+    flags = np.ascontiguousarray(flags, dtype=np.uint8)
+    if k_tile.size != flags.size:
+        raise ValueError("k_tile and flags must have the same length")
+    heads, ps, pw = 0, None, None
+    P64 = ctypes.POINTER(ctypes.c_int64)
+    if sink is not None or window is not None:
+        sink = np.ascontiguousarray(sink, dtype=np.int64)
+        window = np.ascontiguousarray(window, dtype=np.int64)
+        if sink.shape != window.shape or sink.ndim != 1:
+            raise ValueError("sink and window must be 1-D of the same length")
+        heads, ps, pw = sink.size, sink.ctypes.data_as(P64), window.ctypes.data_as(P64)
+    _check(load().tri_attn_check_plan(
+        ctypes.byref(mp), heads, ps, pw, row_ptr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+        row_ptr.size - 1, k_tile.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+        flags.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), k_tile.size))
 
 
 def tri_attn_prefill(t: AttnTensors, mp: MaskParams, d_row_ptr: int, d_k_tile: int,

@@ -163,7 +163,7 @@ using namespace triattn;
 
 extern "C" const char* tri_attn_last_error(void) { return g_error; }
 
-extern "C" int tri_attn_abi_version(void) { return 3; }
+extern "C" int tri_attn_abi_version(void) { return 4; }
 
 extern "C" int tri_attn_prefill(const tri_attn_tensors* t, const tri_mask_params* mp,
                                 const int32_t* d_row_ptr, const int32_t* d_k_tile,
@@ -467,7 +467,8 @@ extern "C" int tri_attn_quantize_k_sizes(const tri_attn_tensors* t, int64_t* k8_
   if (st != TRI_OK) return st;
   if (!k8_bytes || !n_scales) return fail(TRI_ERR_INVALID, "output pointers must be non-NULL");
   *k8_bytes = static_cast<int64_t>(t->batch) * t->heads_kv * t->seqlen * t->head_dim;
-  *n_scales = static_cast<int64_t>(t->batch) * t->heads_kv * ((t->seqlen + 31) / 32);
+  *n_scales = static_cast<int64_t>(t->batch) * t->heads_kv *
+              ((t->seqlen + TRI_KERNEL_BLOCK_K - 1) / TRI_KERNEL_BLOCK_K);
   return TRI_OK;
 }
 
@@ -487,7 +488,8 @@ int quantize_k(const tri_attn_tensors* t, void* d_out, float* d_scale, void* str
   a.heads_kv = t->heads_kv;
   a.head_dim = t->head_dim;
   a.seqlen = static_cast<int32_t>(t->seqlen);
-  a.n_blocks = static_cast<int64_t>(t->batch) * t->heads_kv * ((t->seqlen + 31) / 32);
+  a.n_blocks = static_cast<int64_t>(t->batch) * t->heads_kv *
+               ((t->seqlen + TRI_KERNEL_BLOCK_K - 1) / TRI_KERNEL_BLOCK_K);
   a.k8 = d_out;
   a.scale = d_scale;
   return launch_quantize_k(a, stream);
@@ -504,7 +506,8 @@ extern "C" int tri_attn_quantize_k4_sizes(const tri_attn_tensors* t, int64_t* k4
   if (st != TRI_OK) return st;
   if (!k4_bytes || !n_scales) return fail(TRI_ERR_INVALID, "output pointers must be non-NULL");
   *k4_bytes = static_cast<int64_t>(t->batch) * t->heads_kv * t->seqlen * (t->head_dim / 2);
-  *n_scales = static_cast<int64_t>(t->batch) * t->heads_kv * ((t->seqlen + 31) / 32);
+  *n_scales = static_cast<int64_t>(t->batch) * t->heads_kv *
+              ((t->seqlen + TRI_KERNEL_BLOCK_K - 1) / TRI_KERNEL_BLOCK_K);
   return TRI_OK;
 }
 

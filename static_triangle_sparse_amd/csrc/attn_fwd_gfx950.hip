@@ -588,6 +588,7 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
   // drop the guards of the blocks every wave has
   __builtin_assume(wave >= 0 && wave < kWaves);
   const int N = a.seqlen;
+  const int n_ktiles = (N + kBlockK - 1) / kBlockK;
   const int g = w.h / a.sched.group;
   const int q0 = w.t * kBlockQ;
   const int l32 = lane & 31;
@@ -633,7 +634,7 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
   if constexpr (kTiers) {
     const int64_t bg = static_cast<int64_t>(w.b) * a.sched.heads_kv + g;
     k8base = static_cast<const char*>(a.k8) + bg * N * D;
-    k8scale = reinterpret_cast<const CONST_AS float*>(reinterpret_cast<uintptr_t>(a.k8_scale)) + bg * ((N + kHalf - 1) / kHalf);
+    k8scale = reinterpret_cast<const CONST_AS float*>(reinterpret_cast<uintptr_t>(a.k8_scale)) + bg * n_ktiles;
     low_dist = a.head_low_dist[w.h];
     ln.k8_rd = l32 * C::kK8Stride + ln.hi * 32;
   }
@@ -646,7 +647,7 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
     {
       const int64_t bg = static_cast<int64_t>(w.b) * a.sched.heads_kv + g;
       k4base = static_cast<const char*>(a.k4) + bg * N * (D / 2);
-      k4scale = reinterpret_cast<const CONST_AS float*>(reinterpret_cast<uintptr_t>(a.k4_scale)) + bg * ((N + kHalf - 1) / kHalf);
+      k4scale = reinterpret_cast<const CONST_AS float*>(reinterpret_cast<uintptr_t>(a.k4_scale)) + bg * n_ktiles;
       fp4_dist = a.head_fp4_dist[w.h];
     }
     ln.k4_rd = l32 * C::kK4Stride + ln.hi * 16;
@@ -803,8 +804,9 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
   auto dma = [&](char LDS_AS* stage, int kt, int kb, int tier) __attribute__((always_inline)) {
     const int key0 = kt * kBlockK + kb * kHalf;
     // keys past the sequence end (the second half of a last tile can start
-    // there) are outside the descriptor and land as zeros
-    const int rows = max(N - key0, 0);
+    // there) are outside the descriptor and land as zeros; so does a key tile
+    // outside 0 .. nk - 1 (a malformed list): no byte outside K and V is read
+    const int rows = static_cast<unsigned>(kt) < static_cast<unsigned>(n_ktiles) ? max(N - key0, 0) : 0;
     if (kTiers && tier == 2)
       K::issue_dma_fp4(stage, ln, wave, buffer_rsrc(k4base + static_cast<int64_t>(key0) * (D / 2),
                                                     static_cast<uint32_t>(rows * (D / 2))),
@@ -880,26 +882,26 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
     run(e_split, e_end, 0, high_half);
     __syncthreads();  // all reads of the last stage are done before another walk refills it
   };
-  // score scale of the LOW half starting at key0: s_q times the fp8 K scale
-  // of that half (kept positive so that 0 * -inf never arises: a zero scale
-  // means all-zero codes, whose scores are 0 at any positive scale)
-  // The second half of a last tile can start at or past N: it has no scale
-  // of its own (ceil(N / 32) per head), and all its keys are masked, so it
-  // reads the last one instead of the element past the array.
-  const int last_half = (N + kHalf - 1) / kHalf - 1;
+  // score scale of a LOW key tile starting at key0: s_q times the fp8 K scale
+  // of that tile (kept positive so that 0 * -inf never arises: a zero scale
+  // means all-zero codes, whose scores are 0 at any positive scale); the
+  // index stays inside the ceil(N / 64) scales of the head
+  auto tile_scale = [&](const CONST_AS float* sc, int key0) __attribute__((always_inline)) -> float {
+    return sc[min(max(key0 / kBlockK, 0), n_ktiles - 1)];
+  };
   auto low_sc = [&](int key0) __attribute__((always_inline)) -> float {
-    if constexpr (kTiers) return fmaxf(st.s_q * k8scale[min(key0 / kHalf, last_half)], 1.17549435e-38f);
+    if constexpr (kTiers) return fmaxf(st.s_q * tile_scale(k8scale, key0), 1.17549435e-38f);
     return 1.0f;
   };
   auto fp4_sc = [&](int key0) __attribute__((always_inline)) -> float {
-    if constexpr (kTiers >= 2) return fmaxf(st.s_q4 * k4scale[min(key0 / kHalf, last_half)], 1.17549435e-38f);
+    if constexpr (kTiers >= 2) return fmaxf(st.s_q4 * tile_scale(k4scale, key0), 1.17549435e-38f);
     return 1.0f;
   };
   auto attend_fp4 = [&](const char LDS_AS* stage, int key0, int kb, bool partial) __attribute__((always_inline)) {
-    K::compute_half(stage, ln, st, kb, key0, partial, c_log2, need_ref, true, fp4_sc(key0 + kb * kHalf), true);
+    K::compute_half(stage, ln, st, kb, key0, partial, c_log2, need_ref, true, fp4_sc(key0), true);
   };
   auto attend_low = [&](const char LDS_AS* stage, int key0, int kb, bool partial) __attribute__((always_inline)) {
-    K::compute_half(stage, ln, st, kb, key0, partial, c_log2, need_ref, true, low_sc(key0 + kb * kHalf));
+    K::compute_half(stage, ln, st, kb, key0, partial, c_log2, need_ref, true, low_sc(key0));
   };
   auto attend = [&](const char LDS_AS* stage, int key0, int kb, bool partial) __attribute__((always_inline)) {
     K::compute_half(stage, ln, st, kb, key0, partial, c_log2, need_ref);
@@ -928,10 +930,10 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_kernel(const AttnLaunch 
   if (__syncthreads_or(!(st.l <= kSumLimit))) {
     requant_q();
     walk([&](const char LDS_AS* stage, int key0, int kb, bool partial) __attribute__((always_inline)) {
-           K::max_half(stage, ln, st, kb, key0, partial, true, fp4_sc(key0 + kb * kHalf), true);
+           K::max_half(stage, ln, st, kb, key0, partial, true, fp4_sc(key0), true);
          },
          [&](const char LDS_AS* stage, int key0, int kb, bool partial) __attribute__((always_inline)) {
-           K::max_half(stage, ln, st, kb, key0, partial, true, low_sc(key0 + kb * kHalf));
+           K::max_half(stage, ln, st, kb, key0, partial, true, low_sc(key0));
          },
          reload_q,
          [&](const char LDS_AS* stage, int key0, int kb, bool partial) __attribute__((always_inline)) {

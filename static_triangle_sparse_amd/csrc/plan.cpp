@@ -213,3 +213,75 @@ extern "C" int tri_attn_plan_heads(const tri_mask_params* mp, int32_t heads, con
   }
   return TRI_OK;
 }
+
+// Check of a caller's host plan before its device copy reaches a prefill
+// call: the kernel trusts the arrays it walks.  Row r of the plan lists the
+// key tiles of query tile t = r % nq; with per-head boundaries (heads > 0),
+// head (r / nq) % heads's sink and window define its mask.  Every entry must
+// be a key tile of the row's causal range, in strictly ascending order, that
+// holds a kept pair of the mask, flagged exactly as tri_attn_plan flags it.
+// A plan that lists only some kept tiles (a dynamic selection) passes when
+// each listed tile is valid; a complete static plan is what tri_attn_plan
+// returns.
+extern "C" int tri_attn_check_plan(const tri_mask_params* mp, int32_t heads, const int64_t* sink,
+                                   const int64_t* window, const int32_t* row_ptr, int64_t n_rows,
+                                   const int32_t* k_tile, const uint8_t* flags, int64_t nnz) {
+  clear_error();
+  int st = validate_mask(mp);
+  if (st != TRI_OK) return st;
+  if (heads < 0) return fail(TRI_ERR_INVALID, "heads must be >= 0 (0: one mask for every row)");
+  if (heads > 0 && (!sink || !window))
+    return fail(TRI_ERR_INVALID, "per-head plans need the sink and window arrays");
+  if (heads > 0 && mp->kind != TRI_MASK_TRIANGLE)
+    return fail(TRI_ERR_INVALID, "per-head boundaries apply to the triangle mask");
+  for (int32_t h = 0; h < heads; ++h)
+    if (sink[h] < 0 || window[h] < 1)
+      return fail(TRI_ERR_INVALID, "head %d: sink must be >= 0 and window >= 1", h);
+  if (!row_ptr || (nnz > 0 && (!k_tile || !flags)))
+    return fail(TRI_ERR_INVALID, "row_ptr (and k_tile, flags when nnz > 0) must be non-NULL");
+  const int64_t nq = (mp->seqlen + mp->block_q - 1) / mp->block_q;
+  if (nnz < 0 || n_rows < 0) return fail(TRI_ERR_INVALID, "n_rows and nnz must be >= 0");
+  if (nq == 0 ? n_rows != 0 : n_rows % nq != 0)
+    return fail(TRI_ERR_INVALID, "n_rows %lld is not a multiple of the %lld query tiles",
+                static_cast<long long>(n_rows), static_cast<long long>(nq));
+  if (row_ptr[0] != 0) return fail(TRI_ERR_INVALID, "row_ptr[0] is %d, not 0", row_ptr[0]);
+  if (row_ptr[n_rows] != nnz)
+    return fail(TRI_ERR_INVALID, "row_ptr[%lld] is %d, not nnz = %lld", static_cast<long long>(n_rows),
+                row_ptr[n_rows], static_cast<long long>(nnz));
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const int64_t e0 = row_ptr[r], e1 = row_ptr[r + 1];
+    if (e1 < e0 || e1 > nnz)
+      return fail(TRI_ERR_INVALID, "row_ptr is not non-decreasing within [0, nnz] at row %lld",
+                  static_cast<long long>(r));
+    const int64_t t = r % nq;
+    tri_mask_params m = *mp;
+    if (heads > 0) {
+      const int64_t h = (r / nq) % heads;
+      m.sink = sink[h];
+      m.window = window[h];
+    }
+    const int64_t r1 = std::min(mp->seqlen, (t + 1) * mp->block_q) - 1;
+    TileRange kept[2];
+    const int n_kept = kept_ranges(m, t, kept);
+    for (int64_t e = e0; e < e1; ++e) {
+      const int64_t kt = k_tile[e];
+      if (kt < 0 || kt > r1 / mp->block_k)
+        return fail(TRI_ERR_INVALID, "row %lld entry %lld: key tile %lld is outside 0..%lld",
+                    static_cast<long long>(r), static_cast<long long>(e), static_cast<long long>(kt),
+                    static_cast<long long>(r1 / mp->block_k));
+      if (e > e0 && kt <= k_tile[e - 1])
+        return fail(TRI_ERR_INVALID, "row %lld entry %lld: key tiles are not strictly ascending",
+                    static_cast<long long>(r), static_cast<long long>(e));
+      bool is_kept = false;
+      for (int x = 0; x < n_kept; ++x) is_kept = is_kept || (kt >= kept[x].lo && kt <= kept[x].hi);
+      if (!is_kept)
+        return fail(TRI_ERR_INVALID, "row %lld entry %lld: key tile %lld holds no kept pair",
+                    static_cast<long long>(r), static_cast<long long>(e), static_cast<long long>(kt));
+      if (flags[e] != tile_flag(m, t, kt))
+        return fail(TRI_ERR_INVALID, "row %lld entry %lld: key tile %lld flagged %d, the mask gives %d",
+                    static_cast<long long>(r), static_cast<long long>(e), static_cast<long long>(kt),
+                    flags[e], tile_flag(m, t, kt));
+    }
+  }
+  return TRI_OK;
+}

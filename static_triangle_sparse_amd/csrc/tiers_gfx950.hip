@@ -3,8 +3,9 @@
 // in one normalised output): the fp8 copy of K that the far (LOW) tiles of
 // the tiered attention kernel read.
 //
-// For every (batch, KV head, 32-key half-tile): amax = max |k| over the 32
-// keys (keys >= N excluded), scale = amax / 448, and each value becomes the
+// For every (batch, KV head, key tile of 64 keys, the unit the page assigns a
+// precision to): amax = max |k| over the tile's keys (keys >= N excluded),
+// scale = amax / 448, and each value becomes the
 // e4m3 code of clamp(k * (448 / amax), -448, 448) (round to nearest even,
 // v_cvt_pk_fp8_f32); an all-zero block has scale 0 and zero codes.  A row of
 // D channels is stored as D bytes in the fp8 operand order of the attention
@@ -27,12 +28,12 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kHalfKeys = TRI_KERNEL_BLOCK_K / 2;
+constexpr int kTileKeys = TRI_KERNEL_BLOCK_K;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// One wave per (batch, KV head, half-tile), 4 per workgroup.  Lane l owns
+// One wave per (batch, KV head, key tile), 4 per workgroup.  Lane l owns
 // the 8-channel group m = l % (D / 8) of rows l / (D / 8) + (64 / (D / 8)) i:
 // each load instruction reads whole 2D-byte rows (coalesced), and the 8
 // channels of a group land on 8 consecutive bytes of the fp8 row (4 of the
@@ -41,14 +42,14 @@ template <int D, bool kFp4>
 __global__ __launch_bounds__(256) void quantize_kernel(const QuantLaunch a) {
   constexpr int kGroups = D / 8;                  // 8-channel groups per row
   constexpr int kRowsPerStep = 64 / kGroups;      // rows one load instruction covers
-  constexpr int kSteps = kHalfKeys / kRowsPerStep;
+  constexpr int kSteps = kTileKeys / kRowsPerStep;
   constexpr float kMax = kFp4 ? 6.0f : 448.0f;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t blk = static_cast<int64_t>(blockIdx.x) * 4 + wave;
   if (blk >= a.n_blocks) return;
-  const int nh = (a.seqlen + kHalfKeys - 1) / kHalfKeys;
-  const int hb = static_cast<int>(blk % nh);
-  const int64_t bg = blk / nh;
+  const int nt = (a.seqlen + kTileKeys - 1) / kTileKeys;
+  const int kt = static_cast<int>(blk % nt);
+  const int64_t bg = blk / nt;
   const int b = static_cast<int>(bg / a.heads_kv), g = static_cast<int>(bg % a.heads_kv);
   const int m = lane % kGroups, r0 = lane / kGroups;
   const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.k_stride[0] + g * a.k_stride[1] + 8 * m;
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const QuantLaunch a) {
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < kSteps; ++i) {
-    const int key = hb * kHalfKeys + r0 + kRowsPerStep * i;
+    const int key = kt * kTileKeys + r0 + kRowsPerStep * i;
     u32x4 w = {0u, 0u, 0u, 0u};
     if (key < a.seqlen) w = *reinterpret_cast<const u32x4*>(kp + static_cast<int64_t>(key) * a.k_stride[2]);
     in[i] = w;
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const QuantLaunch a) {
   constexpr int kOutRow = kFp4 ? D / 2 : D;
 #pragma unroll
   for (int i = 0; i < kSteps; ++i) {
-    const int key = hb * kHalfKeys + r0 + kRowsPerStep * i;
+    const int key = kt * kTileKeys + r0 + kRowsPerStep * i;
     if (key >= a.seqlen) continue;
     float v[8];
 #pragma unroll

@@ -162,8 +162,8 @@ struct AttnLaunch {
   const int32_t* head_sink;
   const int32_t* head_window;
   // precision tiers (device; NULL k8 = off): fp8 K [B, Hkv, N, d bytes] in
-  // the fp8 operand channel order, its per-32-key scales [B, Hkv,
-  // ceil(N / 32)], and the per-head LOW boundary [heads_q]
+  // the fp8 operand channel order, its per-key-tile scales [B, Hkv,
+  // ceil(N / 64)], and the per-head LOW boundary [heads_q]
   const void* k8;
   const float* k8_scale;
   const int32_t* head_low_dist;
@@ -233,7 +233,7 @@ struct QuantLaunch {
   const void* k;  // bf16 [B, Hkv, N, d]
   int64_t k_stride[3];
   int32_t heads_kv, head_dim, seqlen;
-  int64_t n_blocks;  // batch * heads_kv * ceil(N / 32)
+  int64_t n_blocks;  // batch * heads_kv * ceil(N / 64): one scale per key tile
   int32_t fp4;       // 0: fp8 copy (d bytes per row), 1: fp4 copy (d / 2 bytes per row)
   void* k8;          // out: fp8 [B, Hkv, N, d bytes] or fp4 [B, Hkv, N, d / 2 bytes]
   float* scale;      // out: [B, Hkv, ceil(N / 32)]

@@ -97,3 +97,35 @@ def sample_rows(N, seed=0, extra_tiles=()):
     tiles = sorted(t for t in tiles if 0 <= t < nq)
     rows = np.concatenate([np.arange(t * 128, min(N, (t + 1) * 128)) for t in tiles])
     return rows
+
+
+def oracle_every_row(bits, mode, kw, o_host, lse_host, chunk=512, what=""):
+    """Check every query row of a layer against the oracle: rows in chunks,
+    each chunk's oracle computed on a worker thread with single-threaded BLAS
+    (the products per 64-row block are small, so threads over chunks use the
+    host cores better than one multi-threaded product at a time).
+    o_host / lse_host: the GPU outputs copied to host (torch CPU tensors).
+    Returns (max |dO|, max rel dLSE) over all rows."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    qb, kb, vb = bits
+    qf, kf, vf = as_f64(qb), as_f64(kb), as_f64(vb)
+    N = qf.shape[2]
+    chunks = [np.arange(s, min(N, s + chunk)) for s in range(0, N, chunk)]
+
+    def one(rows):
+        ro, rl = oatt.attention(qf, kf, vf, mode, kw.get("sink", 0), kw.get("window", 1),
+                                kw.get("last_q", 0), rows=rows)
+        sl = slice(int(rows[0]), int(rows[-1]) + 1)
+        return check(o_host[:, :, sl], lse_host[:, :, sl], ro, rl, f"{what} rows {sl.start}..{sl.stop - 1}")
+
+    workers = max(1, min(16, os.cpu_count() or 1))
+    err = rel = 0.0
+    with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+        for i, (e, r) in enumerate(ex.map(one, chunks)):
+            err, rel = max(err, e), max(rel, r)
+            if (i + 1) % 32 == 0 or i + 1 == len(chunks):
+                note(f"  {what}: {min(N, (i + 1) * chunk)}/{N} rows checked, max|dO|={err:.2e} "
+                     f"max rel dLSE={rel:.2e}")
+    return err, rel

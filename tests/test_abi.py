@@ -32,7 +32,7 @@ def test_header_symbols_are_exported():
     lib = ctypes.CDLL(_abi.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert tsa.tri_attn_abi_version() == 3
+    assert tsa.tri_attn_abi_version() == 4
 
 
 # ----------------------------------------------------------- plan validation
@@ -410,7 +410,7 @@ def test_quantize_k_sizes_and_arguments():
     t = _good_tensors(B=2, Hq=4, Hkv=2, N=1000, d=128)
     nb, ns = ctypes.c_int64(), ctypes.c_int64()
     assert lib.tri_attn_quantize_k_sizes(ctypes.byref(t), ctypes.byref(nb), ctypes.byref(ns)) == tsa.TRI_OK
-    assert nb.value == 2 * 2 * 1000 * 128 and ns.value == 2 * 2 * 32   # ceil(1000 / 32) = 32
+    assert nb.value == 2 * 2 * 1000 * 128 and ns.value == 2 * 2 * 16   # one scale per key tile: ceil(1000 / 64) = 16
     assert tsa.tri_attn_quantize_k_sizes(t) == (nb.value, ns.value)
     assert lib.tri_attn_quantize_k_sizes(ctypes.byref(t), None, ctypes.byref(ns)) == tsa.TRI_ERR_INVALID
     dev = 1 << 24
@@ -423,7 +423,7 @@ def test_quantize_k_sizes_and_arguments():
     assert lib.tri_attn_quantize_k(ctypes.byref(z), dev, dev, None) == tsa.TRI_OK
     # the fp4 copy: half the bytes, the same scales
     assert lib.tri_attn_quantize_k4_sizes(ctypes.byref(t), ctypes.byref(nb), ctypes.byref(ns)) == tsa.TRI_OK
-    assert nb.value == 2 * 2 * 1000 * 64 and ns.value == 2 * 2 * 32
+    assert nb.value == 2 * 2 * 1000 * 64 and ns.value == 2 * 2 * 16
     assert tsa.tri_attn_quantize_k4_sizes(t) == (nb.value, ns.value)
     assert lib.tri_attn_quantize_k4(ctypes.byref(t), None, dev, None) == tsa.TRI_ERR_INVALID
     assert lib.tri_attn_quantize_k4(ctypes.byref(t), dev + 8, dev, None) == tsa.TRI_ERR_INVALID

@@ -8,7 +8,8 @@ GPU takes it in fp32 and the oracle in fp64 on the same bf16 pooled keys, so
 tiles whose oracle score lies within AMBIG (relative to the maximum) of the
 threshold may be decided either way.  Every other tile must agree; every GPU
 list must be valid (ascending, causal range, diagonal tiles present, flags);
-attention is compared on the rows whose lists agree.
+attention is compared on every row against the oracle over the list the GPU
+walked, and on the rows whose lists agree also over the oracle's own list.
 """
 import numpy as np
 import pytest
@@ -100,21 +101,24 @@ def test_pooled_keys_lists_and_attention(dev, N, d, Hq, Hkv, alpha, qscale):
             f" of {p.max_nnz}")
     assert sum(same.values()) >= 0.9 * len(same)
 
-    # attention over the GPU lists vs the oracle over its own lists, on the rows
-    # whose lists agree
+    # attention over the GPU lists: every row against the oracle over the GPU's
+    # own list (a row whose list differs near the threshold is checked too),
+    # and the rows whose lists agree also against the oracle's own list
     o = torch.full((B, Hq, N, d), float("nan"), dtype=torch.float32, device=dev)
     lse = torch.full((B, Hq, N), float("nan"), dtype=torch.float32, device=dev)
     tsa.prefill(q, k, v, mode="lists", plan=p, o_dtype=torch.float32, out=o, lse=lse)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
     ref = odyn.attention_tiles(qf, kf, vf, rrp, rkt)
+    own = odyn.attention_tiles(qf, kf, vf, rp, kt)
     for h in range(Hq):
         ro, rl = ref[(0, h)]
+        go, gl = own[(0, h)]
         for t in range(nq):
-            if not same[h * nq + t]:
-                continue
             rows = slice(t * 128, min(N, (t + 1) * 128))
-            gu.check(o[0, h, rows], lse[0, h, rows], ro[rows], rl[rows], f"h={h} t={t}")
+            gu.check(o[0, h, rows], lse[0, h, rows], go[rows], gl[rows], f"h={h} t={t} (GPU list)")
+            if same[h * nq + t]:
+                gu.check(o[0, h, rows], lse[0, h, rows], ro[rows], rl[rows], f"h={h} t={t}")
 
 
 def test_alpha_zero_lists_are_causal_and_bit_identical_to_dense(dev):
@@ -173,13 +177,14 @@ def test_llama_128k_sampled(dev):
     tsa.prefill(q, k, v, mode="lists", plan=p, o_dtype=torch.bfloat16, out=o, lse=lse)
     torch.cuda.synchronize()
     for (h, t) in [(0, 0), (5, 17), (31, nq - 1), (12, 300)]:
-        if not same[(h, t)]:
-            continue
-        # the oracle's own list of this (head, tile), as a one-head CSR
-        want = wants[(h, t)]
-        one_rp = np.concatenate([np.zeros(t + 1, np.int64), np.full(nq - t, want.size)])
-        ref = odyn.attention_tiles(qf[:, h:h + 1], kf[:, h // 4:h // 4 + 1], vf[:, h // 4:h // 4 + 1],
-                                   one_rp, want, qtiles=[t])
-        ro, rl = ref[(0, 0)]
-        rows = slice(t * 128, (t + 1) * 128)
-        gu.check(o[0, h, rows], lse[0, h, rows], ro, rl, f"128K h={h} t={t}")
+        # the oracle over the list the GPU walked (its own when the two agree),
+        # as a one-head CSR
+        r = h * nq + t
+        lists = [kt[rp[r]:rp[r + 1]]] + ([wants[(h, t)]] if same[(h, t)] else [])
+        for lst in lists:
+            one_rp = np.concatenate([np.zeros(t + 1, np.int64), np.full(nq - t, lst.size)])
+            ref = odyn.attention_tiles(qf[:, h:h + 1], kf[:, h // 4:h // 4 + 1], vf[:, h // 4:h // 4 + 1],
+                                       one_rp, lst, qtiles=[t])
+            ro, rl = ref[(0, 0)]
+            rows = slice(t * 128, (t + 1) * 128)
+            gu.check(o[0, h, rows], lse[0, h, rows], ro, rl, f"128K h={h} t={t}")

@@ -1,7 +1,9 @@
 """Parity at the full benchmark sizes (Llama-3-8B-shaped layer: 32 query heads,
 8 KV heads, head_dim 128; sink 128, window 2048, last-Q 128) in the launch
 configuration the benchmark times (bf16 O plus f32 LSE on the current
-stream), on sampled query tiles the oracle computes row by row."""
+stream): every row of the 32K and 128K triangle layers against the oracle,
+and sampled query tiles of the dense layers (whose rows cost O(N) keys
+each) and of the stack layer shapes."""
 import numpy as np
 import pytest
 import torch
@@ -16,6 +18,19 @@ KW = dict(sink=128, window=2048, last_q=128)
 @pytest.fixture(scope="module")
 def dev():
     return gu.require_gpu()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("N", [32768, 131072])
+def test_llama_triangle_layer_every_row(dev, N):
+    gu.note(f"llama triangle layer N={N}, every row: inputs and kernel")
+    bits, (q, k, v) = gu.make_inputs(0, 1, 32, 8, N, 128, dev)
+    o, lse = gu.run(q, k, v, "triangle", o_dtype=torch.bfloat16, **KW)
+    o_h, l_h = o.cpu(), lse.cpu()
+    del o, lse, q, k, v
+    torch.cuda.empty_cache()
+    err, rel = gu.oracle_every_row(bits, "triangle", KW, o_h, l_h, what=f"N={N} triangle")
+    gu.note(f"  every row of N={N}: max|dO|={err:.2e} max rel dLSE={rel:.2e}")
 
 
 @pytest.mark.parametrize("N", [32768, 131072])

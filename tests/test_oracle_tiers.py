@@ -73,7 +73,7 @@ def test_no_low_tiles_is_the_triangle_attention():
 
 
 def test_exactly_representable_inputs_make_fp8_tiles_exact():
-    # entries in {-1.75, 0, 1.75} with every row and half-tile reaching 1.75:
+    # entries in {-1.75, 0, 1.75} with every row and key tile reaching 1.75:
     # 448 / 1.75 = 256 and 1.75 / 448 = 2^-8 are exact in float32, and every
     # scaled value is +-448 or 0 (exact codes), so the fp8 scores are exact
     N, d = 400, 8
@@ -104,8 +104,8 @@ def test_mixed_tiers_against_a_scalar_brute_force():
             s_q = float(amax / np.float32(448))
             z = []
             for j in js:
-                c0 = (j // 8) * 8                        # the 8-key half of its 16-key tile
-                blk = np.asarray(k[0, 0, c0:c0 + 8], np.float32)
+                c0 = (j // 16) * 16                      # its 16-key tile
+                blk = np.asarray(k[0, 0, c0:c0 + 16], np.float32)
                 bmax = np.float32(np.max(np.abs(blk)))
                 k8 = tiers.round_e4m3((np.asarray(k[0, 0, j], np.float32) *
                                        (np.float32(448) / bmax)).astype(np.float32))
@@ -168,7 +168,7 @@ def test_fp4_tier_absent_or_unreached_is_the_two_tier_layer():
 
 
 def test_exactly_representable_inputs_make_fp4_tiles_exact():
-    # entries in {-a, 0, a} with every row and half-tile reaching a: every
+    # entries in {-a, 0, a} with every row and key tile reaching a: every
     # scaled value is +-6 or 0 (exact codes) and 6 / a, a / 6 are exact for
     # a = 1.5 (4 and 0.25), so the fp4 scores are exact
     N, d = 400, 8
@@ -211,8 +211,8 @@ def test_three_tiers_against_a_scalar_brute_force():
                     z.append(scale * math.fsum(q[0, h, i, c] * k[0, 0, j, c] for c in range(d)))
                     continue
                 qc, s_q = q_code(row, top, rnd)
-                c0 = (j // 8) * 8
-                blk = np.asarray(k[0, 0, c0:c0 + 8], np.float32)
+                c0 = (j // 16) * 16
+                blk = np.asarray(k[0, 0, c0:c0 + 16], np.float32)
                 bmax = np.float32(np.max(np.abs(blk)))
                 kc = rnd((np.asarray(k[0, 0, j], np.float32) * (np.float32(top) / bmax)).astype(np.float32))
                 s_k = float(bmax / np.float32(top))
