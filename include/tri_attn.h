@@ -23,8 +23,9 @@
  *   - All argument validation happens before any HIP runtime call, so every
  *     error path can be exercised on a machine without a GPU.
  *   - The library never allocates, frees or copies device memory and keeps no
- *     global state other than the per-thread error message.  The caller owns
- *     every buffer, host or device.
+ *     global state other than the per-thread error message and the scratch
+ *     array of tri_dyn_plan_noalloc (one per GPU, in the code object).  The
+ *     caller owns every other buffer, host or device.
  *   - Device calls enqueue on the caller's stream and return; results are
  *     bit-deterministic for identical inputs (fixed traversal order, no
  *     atomics).  Device faults surface at the caller's next synchronisation.
@@ -211,6 +212,25 @@ int tri_dyn_plan_sizes(const tri_attn_tensors* t, int64_t* workspace_bytes, int6
 int tri_dyn_plan(const tri_attn_tensors* t, const tri_dyn_params* dp, void* d_workspace,
                  int64_t workspace_bytes, int32_t* d_row_ptr, int32_t* d_k_tile, uint8_t* d_flags,
                  int64_t capacity, void* stream);
+
+/*
+ * tri_dyn_plan_noalloc -- tri_dyn_plan for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The workspace is a library-owned device
+ * array of TRI_DYN_SCRATCH_BYTES per GPU (each GPU the library runs on holds
+ * it until the process ends); the call allocates nothing and the caller
+ * passes only the outputs (as for tri_dyn_plan).  The array of the current
+ * device is used (`stream` must belong to it).  A layer whose workspace
+ * (tri_dyn_plan_sizes) exceeds TRI_DYN_SCRATCH_BYTES is rejected with
+ * TRI_ERR_CAPACITY before any HIP call (64 MiB covers e.g. 32 query / 8 KV
+ * heads, d = 128, up to N = 262144 at batch 1).  Every call on one GPU
+ * shares that GPU's array and leaves its contents behind (nothing in it
+ * needs to start at zero): calls that overlap on one GPU -- on two streams,
+ * or from two threads -- race and must be serialised by the caller.
+ */
+enum { TRI_DYN_SCRATCH_BYTES = 64 << 20 };
+int tri_dyn_plan_noalloc(const tri_attn_tensors* t, const tri_dyn_params* dp, int32_t* d_row_ptr,
+                         int32_t* d_k_tile, uint8_t* d_flags, int64_t capacity, void* stream);
 
 /*
  * tri_attn_prefill_lists -- the attention kernel walking per-(batch, head)

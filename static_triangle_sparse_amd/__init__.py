@@ -29,7 +29,7 @@ from ._abi import (  # noqa: F401
     tri_attn_quantize_k, tri_attn_quantize_k_sizes, tri_attn_work_item, tri_dyn_plan,
     tri_dyn_plan_sizes, tri_attn_prefill_split, tri_attn_split_work_item,
     tri_attn_split_workspace_size, tri_attn_quantize_k4, tri_attn_quantize_k4_sizes,
-    tri_attn_check_plan,
+    tri_attn_check_plan, tri_dyn_plan_noalloc, TRI_DYN_SCRATCH_BYTES,
 )
 
 __all__ = [
@@ -39,7 +39,7 @@ __all__ = [
     "HeadPlan", "head_plan", "tri_attn_plan_heads", "tri_attn_prefill_heads",
     "QuantizedK", "quantize_k", "tri_attn_quantize_k", "tri_attn_prefill_tiered",
     "split_workspace", "tri_attn_prefill_split", "tri_attn_split_workspace_size",
-    "tri_attn_check_plan", "stack_prefill",
+    "tri_attn_check_plan", "stack_prefill", "tri_dyn_plan_noalloc",
 ]
 
 _WORKSPACE = {}

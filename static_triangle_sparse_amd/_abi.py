@@ -31,6 +31,7 @@ TRI_TILE_PARTIAL = 1
 TRI_KERNEL_BLOCK_Q = 128
 TRI_KERNEL_BLOCK_K = 64
 TRI_DYN_PROBES = 16
+TRI_DYN_SCRATCH_BYTES = 64 << 20
 
 _STATUS_NAMES = {
     TRI_OK: "TRI_OK", TRI_ERR_INVALID: "TRI_ERR_INVALID", TRI_ERR_CAPACITY: "TRI_ERR_CAPACITY",
@@ -129,6 +130,9 @@ def load() -> ctypes.CDLL:
                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                  ctypes.c_void_p]
     lib.tri_dyn_plan.restype = ctypes.c_int
+    lib.tri_dyn_plan_noalloc.argtypes = [P(AttnTensors), P(DynParams), ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.tri_dyn_plan_noalloc.restype = ctypes.c_int
     lib.tri_attn_prefill_lists.argtypes = [P(AttnTensors), ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_void_p]
     lib.tri_attn_prefill_lists.restype = ctypes.c_int
@@ -277,6 +281,15 @@ def tri_dyn_plan(t: AttnTensors, alpha: float, d_workspace: int, workspace_bytes
     dp = DynParams(float(alpha), int(n_probe))
     _check(load().tri_dyn_plan(ctypes.byref(t), ctypes.byref(dp), d_workspace, workspace_bytes,
                                d_row_ptr, d_k_tile, d_flags, capacity, stream))
+
+
+def tri_dyn_plan_noalloc(t: AttnTensors, alpha: float, d_row_ptr: int, d_k_tile: int, d_flags: int,
+                         capacity: int, stream: int, n_probe: int = TRI_DYN_PROBES) -> None:
+    """tri_dyn_plan with the library-owned workspace (no allocation); device
+    output pointers as for tri_dyn_plan."""
+    dp = DynParams(float(alpha), int(n_probe))
+    _check(load().tri_dyn_plan_noalloc(ctypes.byref(t), ctypes.byref(dp), d_row_ptr, d_k_tile, d_flags,
+                                       capacity, stream))
 
 
 def tri_attn_prefill_lists(t: AttnTensors, d_row_ptr: int, d_k_tile: int, d_flags: int,

@@ -243,10 +243,12 @@ extern "C" int tri_dyn_plan_sizes(const tri_attn_tensors* t, int64_t* workspace_
   return TRI_OK;
 }
 
-extern "C" int tri_dyn_plan(const tri_attn_tensors* t, const tri_dyn_params* dp, void* d_workspace,
-                            int64_t workspace_bytes, int32_t* d_row_ptr, int32_t* d_k_tile,
-                            uint8_t* d_flags, int64_t capacity, void* stream) {
-  clear_error();
+namespace {
+
+// Validation of a dynamic plan's arguments except the workspace; fills the
+// launch description (workspace pointers left unset).
+int dyn_prepare(const tri_attn_tensors* t, const tri_dyn_params* dp, int32_t* d_row_ptr, int32_t* d_k_tile,
+                uint8_t* d_flags, int64_t capacity, DynLaunch* a, DynWorkspace* ws) {
   int st = validate_tensors(t);
   if (st != TRI_OK) return st;
   if (!dp) return fail(TRI_ERR_INVALID, "dynamic-plan parameters pointer is NULL");
@@ -259,45 +261,82 @@ extern "C" int tri_dyn_plan(const tri_attn_tensors* t, const tri_dyn_params* dp,
   const int64_t nkt = (N + TRI_KERNEL_BLOCK_K - 1) / TRI_KERNEL_BLOCK_K;
   const int64_t rows = static_cast<int64_t>(t->batch) * t->heads_q * nq;
   const int64_t need = static_cast<int64_t>(t->batch) * t->heads_q * causal_tiles(N);
-  const DynWorkspace ws = dyn_workspace(t->batch, t->heads_q, t->heads_kv, t->head_dim, N);
+  *ws = dyn_workspace(t->batch, t->heads_q, t->heads_kv, t->head_dim, N);
   if (need >= INT32_MAX || rows >= INT32_MAX)
     return fail(TRI_ERR_UNSUPPORTED, "list sizes exceed 2^31-1 entries");
-  if (!d_workspace || !d_row_ptr || !d_k_tile || !d_flags)
-    return fail(TRI_ERR_INVALID, "workspace and output pointers must be non-NULL");
-  if (!aligned(d_workspace, 256)) return fail(TRI_ERR_INVALID, "workspace must be 256-byte aligned");
+  if (!d_row_ptr || !d_k_tile || !d_flags)
+    return fail(TRI_ERR_INVALID, "output pointers must be non-NULL");
   if (!aligned(d_row_ptr, 4) || !aligned(d_k_tile, 4))
     return fail(TRI_ERR_INVALID, "row_ptr and k_tile must be 4-byte aligned");
-  if (workspace_bytes < ws.total)
-    return fail(TRI_ERR_CAPACITY, "workspace of %lld bytes, %lld needed",
-                static_cast<long long>(workspace_bytes), static_cast<long long>(ws.total));
   if (capacity < need)
     return fail(TRI_ERR_CAPACITY, "list capacity %lld, %lld needed", static_cast<long long>(capacity),
                 static_cast<long long>(need));
-  if (N == 0) return TRI_OK;
-  DynLaunch a{};
-  a.q = t->q;
-  a.k = t->k;
-  memcpy(a.q_stride, t->q_stride, sizeof(a.q_stride));
-  memcpy(a.k_stride, t->k_stride, sizeof(a.k_stride));
-  a.batch = t->batch;
-  a.heads_q = t->heads_q;
-  a.heads_kv = t->heads_kv;
-  a.head_dim = t->head_dim;
-  a.seqlen = static_cast<int32_t>(N);
-  a.nq = static_cast<int32_t>(nq);
-  a.nkt = static_cast<int32_t>(nkt);
-  a.words = static_cast<int32_t>((nkt + 31) / 32);
-  a.n_rows = rows;
-  a.n_pool_tiles = static_cast<int64_t>(t->batch) * t->heads_kv * nkt;
-  a.scale = t->softmax_scale;
-  a.alpha = dp->alpha;
-  char* w = static_cast<char*>(d_workspace);
-  a.pooled = w + ws.pooled;
-  a.bitmap = reinterpret_cast<uint32_t*>(w + ws.bitmap);
-  a.counts = reinterpret_cast<int32_t*>(w + ws.counts);
-  a.row_ptr = d_row_ptr;
-  a.k_tile = d_k_tile;
-  a.flags = d_flags;
+  *a = DynLaunch{};
+  a->q = t->q;
+  a->k = t->k;
+  memcpy(a->q_stride, t->q_stride, sizeof(a->q_stride));
+  memcpy(a->k_stride, t->k_stride, sizeof(a->k_stride));
+  a->batch = t->batch;
+  a->heads_q = t->heads_q;
+  a->heads_kv = t->heads_kv;
+  a->head_dim = t->head_dim;
+  a->seqlen = static_cast<int32_t>(N);
+  a->nq = static_cast<int32_t>(nq);
+  a->nkt = static_cast<int32_t>(nkt);
+  a->words = static_cast<int32_t>((nkt + 31) / 32);
+  a->n_rows = rows;
+  a->n_pool_tiles = static_cast<int64_t>(t->batch) * t->heads_kv * nkt;
+  a->scale = t->softmax_scale;
+  a->alpha = dp->alpha;
+  a->row_ptr = d_row_ptr;
+  a->k_tile = d_k_tile;
+  a->flags = d_flags;
+  return TRI_OK;
+}
+
+void dyn_set_workspace(DynLaunch* a, const DynWorkspace& ws, void* base) {
+  char* w = static_cast<char*>(base);
+  a->pooled = w + ws.pooled;
+  a->bitmap = reinterpret_cast<uint32_t*>(w + ws.bitmap);
+  a->counts = reinterpret_cast<int32_t*>(w + ws.counts);
+}
+
+}  // namespace
+
+extern "C" int tri_dyn_plan(const tri_attn_tensors* t, const tri_dyn_params* dp, void* d_workspace,
+                            int64_t workspace_bytes, int32_t* d_row_ptr, int32_t* d_k_tile,
+                            uint8_t* d_flags, int64_t capacity, void* stream) {
+  clear_error();
+  DynLaunch a;
+  DynWorkspace ws;
+  int st = dyn_prepare(t, dp, d_row_ptr, d_k_tile, d_flags, capacity, &a, &ws);
+  if (st != TRI_OK) return st;
+  if (!d_workspace) return fail(TRI_ERR_INVALID, "workspace pointer must be non-NULL");
+  if (!aligned(d_workspace, 256)) return fail(TRI_ERR_INVALID, "workspace must be 256-byte aligned");
+  if (workspace_bytes < ws.total)
+    return fail(TRI_ERR_CAPACITY, "workspace of %lld bytes, %lld needed",
+                static_cast<long long>(workspace_bytes), static_cast<long long>(ws.total));
+  if (t->seqlen == 0) return TRI_OK;
+  dyn_set_workspace(&a, ws, d_workspace);
+  return launch_dyn_plan(a, stream);
+}
+
+extern "C" int tri_dyn_plan_noalloc(const tri_attn_tensors* t, const tri_dyn_params* dp, int32_t* d_row_ptr,
+                                    int32_t* d_k_tile, uint8_t* d_flags, int64_t capacity, void* stream) {
+  clear_error();
+  DynLaunch a;
+  DynWorkspace ws;
+  int st = dyn_prepare(t, dp, d_row_ptr, d_k_tile, d_flags, capacity, &a, &ws);
+  if (st != TRI_OK) return st;
+  if (ws.total > TRI_DYN_SCRATCH_BYTES)
+    return fail(TRI_ERR_CAPACITY,
+                "the layer needs %lld bytes of workspace; the library-owned scratch holds %lld "
+                "(use tri_dyn_plan with a caller workspace)",
+                static_cast<long long>(ws.total), static_cast<long long>(TRI_DYN_SCRATCH_BYTES));
+  if (t->seqlen == 0) return TRI_OK;
+  void* base = nullptr;
+  if ((st = dyn_scratch(&base)) != TRI_OK) return st;
+  dyn_set_workspace(&a, ws, base);
   return launch_dyn_plan(a, stream);
 }
 

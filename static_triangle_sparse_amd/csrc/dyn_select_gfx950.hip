@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "tri_attn_internal.h"
 
 namespace triattn {
@@ -391,7 +393,35 @@ int launch_d(const DynLaunch& a, hipStream_t stream) {
   return TRI_OK;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+// Workspace of tri_dyn_plan_noalloc: one array per GPU the library runs on,
+// held until the process ends.  In host code `scratch` names a host-side
+// stand-in; the device address of each GPU's copy comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is handed to kernels.
+static __device__ __align__(256) char scratch[TRI_DYN_SCRATCH_BYTES];
+
+int dyn_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return fail(TRI_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(err));
+  if (dev < 0 || dev >= kMaxDevices) return fail(TRI_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || !p)
+      return fail(TRI_ERR_HIP, "hipGetSymbolAddress of the scratch array failed: %s", hipGetErrorString(err));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return TRI_OK;
+}
 
 int launch_dyn_plan(const DynLaunch& a, void* stream) {
   const hipStream_t s = static_cast<hipStream_t>(stream);

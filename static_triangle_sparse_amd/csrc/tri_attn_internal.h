@@ -227,6 +227,10 @@ DynWorkspace dyn_workspace(int64_t batch, int64_t heads_q, int64_t heads_kv, int
 // Enqueue the four launches of the dynamic plan; returns TRI_OK or TRI_ERR_HIP.
 int launch_dyn_plan(const DynLaunch& a, void* stream);
 
+// Device address of the current GPU's library-owned workspace of
+// TRI_DYN_SCRATCH_BYTES (tri_dyn_plan_noalloc); TRI_OK or TRI_ERR_HIP.
+int dyn_scratch(void** ptr);
+
 // ---------------------------------------------------------------- precision tiers
 
 struct QuantLaunch {

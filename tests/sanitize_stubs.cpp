@@ -9,4 +9,5 @@ int launch_attn_fwd(const AttnLaunch&, void*) { return fail(TRI_ERR_HIP, "host-o
 int launch_split_merge(const AttnLaunch&, void*) { return fail(TRI_ERR_HIP, "host-only build: no device code"); }
 int launch_dyn_plan(const DynLaunch&, void*) { return fail(TRI_ERR_HIP, "host-only build: no device code"); }
 int launch_quantize_k(const QuantLaunch&, void*) { return fail(TRI_ERR_HIP, "host-only build: no device code"); }
+int dyn_scratch(void**) { return fail(TRI_ERR_HIP, "host-only build: no device code"); }
 }  // namespace triattn

@@ -217,6 +217,38 @@ def test_dyn_plan_rejects_bad_arguments():
     assert call(tt=z, wbytes=ws0, cap=nnz0) == tsa.TRI_OK
 
 
+def test_dyn_plan_noalloc_rejects_bad_arguments():
+    # every rejection happens before any HIP call (no GPU here)
+    lib = _abi.load()
+    t = _good_tensors(N=1000)
+    ws, rows, nnz = tsa.tri_dyn_plan_sizes(t)
+    assert ws <= tsa.TRI_DYN_SCRATCH_BYTES
+    P = 1 << 27
+
+    def call(alpha=0.5, n_probe=16, rp=P, kt=P, fl=P, cap=nnz, tt=t):
+        dp = tsa.DynParams(alpha, n_probe)
+        return lib.tri_dyn_plan_noalloc(ctypes.byref(tt) if tt is not None else None, ctypes.byref(dp),
+                                        rp, kt, fl, cap, None)
+
+    assert call(tt=None) == tsa.TRI_ERR_INVALID
+    assert call(alpha=2.0) == tsa.TRI_ERR_INVALID
+    assert call(n_probe=4) == tsa.TRI_ERR_UNSUPPORTED
+    assert call(rp=None) == tsa.TRI_ERR_INVALID
+    assert call(kt=P + 2) == tsa.TRI_ERR_INVALID
+    assert call(cap=nnz - 1) == tsa.TRI_ERR_CAPACITY
+    # a layer whose workspace exceeds the library-owned array
+    big = _good_tensors(N=1 << 19, Hq=32, Hkv=8)
+    wsb, _, nnzb = tsa.tri_dyn_plan_sizes(big)
+    assert wsb > tsa.TRI_DYN_SCRATCH_BYTES
+    assert call(tt=big, cap=nnzb) == tsa.TRI_ERR_CAPACITY
+    assert "scratch" in tsa.last_error()
+    # the largest Llama-shaped layer it holds: N = 262144
+    edge = _good_tensors(N=1 << 18, Hq=32, Hkv=8)
+    assert tsa.tri_dyn_plan_sizes(edge)[0] <= tsa.TRI_DYN_SCRATCH_BYTES
+    z = _good_tensors(N=0)
+    assert call(tt=z, cap=tsa.tri_dyn_plan_sizes(z)[2]) == tsa.TRI_OK
+
+
 def test_prefill_lists_rejects_bad_arguments():
     lib = _abi.load()
     t = _good_tensors()
