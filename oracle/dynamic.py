@@ -95,7 +95,7 @@ def tile_scores(q_rows, kbar, rows, last_row, scale, block_k=64):
 
 
 def select_tiles(q, k, alpha, scale=None, block_q=128, block_k=64, n_probe=N_PROBE,
-                 return_scores=False):
+                 return_scores=False, pooled_bf16=True):
     """Per-(batch, head) kept-tile lists of a dense layer.
 
     q [B, Hq, N, d], k [B, Hkv, N, d].  Returns CSR over rows
@@ -109,7 +109,7 @@ def select_tiles(q, k, alpha, scale=None, block_q=128, block_k=64, n_probe=N_PRO
     G = Hq // Hkv
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    kbar = pooled_keys(k, block_k)
+    kbar = pooled_keys(k, block_k, to_bf16=pooled_bf16)
     nq = -(-N // block_q)
     row_ptr = [0]
     k_tile, flags, scores = [], [], []

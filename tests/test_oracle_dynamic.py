@@ -228,3 +228,24 @@ def test_brute_attention_agrees_on_causal_lists():
     for h in range(2):
         assert np.allclose(got[(0, h)][0], np.asarray(bo[0][h]), rtol=0, atol=1e-12)
         assert np.allclose(got[(0, h)][1], np.asarray(bl[0][h]), rtol=0, atol=1e-12)
+
+
+def test_bf16_pooled_keys_move_only_near_threshold_decisions():
+    # The pooled keys are rounded to bf16 (the precision the selection's
+    # products take them in): a reading of where the decision is taken, not
+    # of what is selected.  Against fp64 pooled keys, every tile decided
+    # differently must lie within 2% of its threshold, and almost all lists
+    # are unchanged.
+    q, k, _ = _inputs(77, 1, 4, 2, 3000, 64)
+    q = q * 4.0
+    rp_b, kt_b, _, sc_b = dyn.select_tiles(q, k, 0.5, return_scores=True)
+    rp_f, kt_f, _, sc_f = dyn.select_tiles(q, k, 0.5, return_scores=True, pooled_bf16=False)
+    same = 0
+    for r in range(rp_b.size - 1):
+        a = set(kt_b[rp_b[r]:rp_b[r + 1]].tolist())
+        b = set(kt_f[rp_f[r]:rp_f[r + 1]].tolist())
+        s, thr = sc_f[r]
+        for t in a ^ b:
+            assert abs(s[t] - thr) <= 0.02 * thr, (r, t, s[t], thr)
+        same += a == b
+    assert same >= 0.9 * (rp_b.size - 1)
