@@ -19,7 +19,9 @@
 // walks.
 //
 // Four launches: pool (mean keys), select (scores -> keep bitmap + count per
-// row), scan (counts -> row pointers), emit (bitmap -> list).
+// row), scan (counts -> row pointers), emit (bitmap -> list).  The select
+// computes each probe logit twice (softmax sums, then scores); the keep
+// decisions read the scores back from LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,6 +35,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBq = TRI_KERNEL_BLOCK_Q;
 constexpr int kBk = TRI_KERNEL_BLOCK_K;
@@ -76,245 +79,379 @@ __global__ __launch_bounds__(256) void dyn_pool_kernel(const DynLaunch a) {
 }
 
 // ---------------------------------------------------------------- select
-// One workgroup (4 waves) per (batch, query head, pair of query tiles t0 =
-// 2u, t1 = 2u + 1).  Scores come from v_mfma_f32_32x32x16_bf16 with the 32
-// probes of the pair as the A rows (rows 0..15: t0, rows 16..31: t1; rows of
-// a missing tile or a probe >= N are zero) and the pooled keys of 32 tiles as
-// the B columns: lane l then holds tile kt0 + l % 32, and register r holds
-// row 8 (r >> 2) + 4 (l >> 5) + (r & 3) -- registers 0..7 probes of t0,
-// 8..15 probes of t1.  Wave w takes the 32-tile groups w, w + 4, ..., with the
-// next group's pooled keys loaded while the current one is scored.  Three
-// passes recompute the scores: per-probe softmax max and sum, the maximum
-// tile score of each query tile, the keep bits (one 32-bit word per group
-// and query tile).
+// One workgroup (4 waves) per (batch, query head, group of kQT = 4
+// consecutive query tiles t0 .. t0 + 3); blocks run the heaviest group (the
+// most candidate tiles) first, and consecutive blocks cycle through the KV
+// heads.  Every pooled key a workgroup reads scores the probes of all four
+// query tiles, so the keys cross the L2 once per 64 probes.  Scores come from
+// v_mfma_f32_16x16x32_bf16 on mini-groups of 16 key tiles: block rb of the A
+// operand holds the 16 probes of query tile t0 + rb (zero rows for a missing
+// tile or a probe >= N), the B operand the pooled keys of the 16 tiles; lane
+// l then holds tile kt0 + l % 16 and, in register r of block rb, probe
+// 4 (l / 16) + r of that query tile.  Wave w takes the mini-groups w, w + 4,
+// ..., two at a time from two key buffers, each reloaded for the mini-group
+// two steps on right after its use.
+//
+// The softmax of probe p over the tiles it sees is taken against one
+// reference per probe, its logit on key tile 0 (every probe sees tile 0):
+//   pass 1: l_p = sum over tiles of exp2(c z - c ref_p), summed over the
+//           lanes and waves directly (one reference per probe);
+//   pass 2: score(t, kt) = sum over the probes p of t of
+//           exp2(c z - c ref_p - log2 l_p), written to LDS, and its maximum;
+//   keep:   bits from the LDS scores (score >= alpha * max, or the tile
+//           crosses the diagonal), one 32-bit word per 32 tiles and query tile.
+// Softmax does not depend on the reference point, so this is the softmax of
+// the definition.  A logit more than 64 / c above its reference (exp2
+// range) sends the workgroup through an exact-max pass first, which makes
+// the per-probe maximum the reference.  Layers with more candidate tiles
+// than the LDS score buffer holds recompute the scores for the keep bits.
+constexpr int kQT = 4;                // query tiles per workgroup
+constexpr int kLdsScoreTiles = 4096;  // 64 KiB of scores (four query tiles)
+constexpr float kRefMargin = 64.0f;   // log2 units a logit may exceed its reference by
+constexpr int kMg = 16;               // key tiles per mini-group
+constexpr int kPr = 4 * kQT;          // probe registers per lane
+
 template <int D>
 struct Select {
-  static constexpr int kSteps = D / 16;
+  static constexpr int kSteps = D / 32;  // k-steps of 32 channels
 
   struct Ctx {
-    bf16x8 q[kSteps];    // probe operand (A)
-    int probe_row[16];   // row of register r's probe (INT32_MIN: none)
-    const uint16_t* kbar;  // pooled keys of the query's KV head
-    int nc;              // candidate key tiles (of the later tile of the pair)
-    float c;             // scale * log2(e)
-    int l32, hi;
+    bf16x8 q[kQT][kSteps];  // probe operand (A), block rb = query tile t0 + rb
+    const uint16_t* kbar;   // pooled keys of the query's KV head
+    int nc;                 // candidate key tiles (of the last tile of the group)
+    int t0;                 // first query tile of the group
+    int n_qt;               // query tiles of the group that exist
+    int n;                  // N
+    float c;                // scale * log2(e)
+    int col, quad;          // lane % 16 (tile), lane / 16 (probe quad)
   };
 
   struct Keys {
     u32x4 w[kSteps];
   };
 
+  // Keys of tiles kt0 + col; a tile past the candidates reads the last
+  // candidate instead (its logits are masked to -inf), so that the loads
+  // carry no branch and the walk's waits can count them exactly.
   static __device__ __forceinline__ Keys load(const Ctx& cx, int kt0) {
     Keys k;
-    const int kt = kt0 + cx.l32;
+    const int kt = min(kt0 + cx.col, cx.nc - 1);
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (kt < cx.nc)
-        w = *reinterpret_cast<const u32x4*>(cx.kbar + static_cast<int64_t>(kt) * D + s * 16 + cx.hi * 8);
-      k.w[s] = w;
-    }
+    for (int s = 0; s < kSteps; ++s)
+      k.w[s] = *reinterpret_cast<const u32x4*>(cx.kbar + static_cast<int64_t>(kt) * D + s * 32 + cx.quad * 8);
     return k;
   }
 
-  // z (log2 units) of this lane's 16 probes against tile kt0 + l32; -inf where
-  // the probe does not exist or does not see the tile
-  static __device__ __forceinline__ void logits(const Ctx& cx, const Keys& k, int kt0, float (&z)[16]) {
-    const int kt = kt0 + cx.l32;
-    f32x16 acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  // Pooled key of tile 0 in every column: each lane's registers then hold
+  // its probes' logits on tile 0.
+  static __device__ __forceinline__ Keys load_tile0(const Ctx& cx) {
+    Keys k;
 #pragma unroll
     for (int s = 0; s < kSteps; ++s)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cx.q[s], __builtin_bit_cast(bf16x8, k.w[s]), acc, 0, 0, 0);
+      k.w[s] = *reinterpret_cast<const u32x4*>(cx.kbar + s * 32 + cx.quad * 8);
+    return k;
+  }
+
+  // raw logits <q_p, kbar> (scale not applied): z[4 rb + r]
+  static __device__ __forceinline__ void raw(const Ctx& cx, const Keys& k, float (&z)[kPr]) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const bool sees = kt < cx.nc && kt * kBk <= cx.probe_row[r];
-      z[r] = sees ? acc[r] * cx.c : -INFINITY;
+    for (int rb = 0; rb < kQT; ++rb) {
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cx.q[rb][s], __builtin_bit_cast(bf16x8, k.w[s]), acc, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) z[4 * rb + r] = acc[r];
     }
   }
 
-  // Score of this lane's tile for the probes in registers r0 .. r0 + 7: sum
-  // of exp2(z - m) / l.  Contraction is off so that every pass computes
-  // bit-identical scores.
-  static __device__ __forceinline__ float partial_score(const float (&z)[16], const float (&m)[16],
-                                                        const float (&inv_l)[16], int r0) {
-#pragma clang fp contract(off)
-    float e[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-      e[r] = z[r0 + r] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(z[r0 + r] - m[r0 + r]) * inv_l[r0 + r];
-    return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+  // probe (0 .. 16 kQT - 1 over the group) and row of register x = 4 rb + r
+  static __device__ __forceinline__ int probe_of(const Ctx& cx, int x) { return 16 * (x >> 2) + 4 * cx.quad + (x & 3); }
+  static __device__ __forceinline__ int row_of(const Ctx& cx, int x) {
+    return (cx.t0 + (x >> 2)) * kBq + (4 * cx.quad + (x & 3)) * kProbeStep;
+  }
+  // the probe of register x exists (its query tile exists, its row < N)
+  static __device__ __forceinline__ bool probe_exists(const Ctx& cx, int x) {
+    return (x >> 2) < cx.n_qt && row_of(cx, x) < cx.n;
   }
 
-  // Walk this wave's groups with the next group's keys in flight.
+  // Raw logits z of a mini-group (the caller forms c z - c ref with one
+  // fma), -inf where the probe does not exist or does not see the tile
+  // (64 kt > its row) or the tile is past the candidates.  Only mini-groups
+  // near the diagonal or the end need the test; elsewhere a probe that does
+  // not exist (zero query) has z = 0 and weight 0 (its reference is -inf in
+  // the score pass).
+  static __device__ __forceinline__ void logits(const Ctx& cx, const Keys& k, int kt0, float (&z)[kPr]) {
+    raw(cx, k, z);
+    const bool clear = kt0 + kMg - 1 < cx.nc && (kt0 + kMg - 1) * kBk <= cx.t0 * kBq;
+    if (!clear) {
+      const int kt = kt0 + cx.col;
+#pragma unroll
+      for (int x = 0; x < kPr; ++x)
+        z[x] = (probe_exists(cx, x) && kt < cx.nc && kt * kBk <= row_of(cx, x)) ? z[x] : -INFINITY;
+    }
+  }
+
+  // Walk this wave's mini-groups (gi = wave, wave + 4, ...) two at a time,
+  // each of two key buffers reloaded right after its use for the mini-group
+  // two steps on.  Fixed buffers and unconditional loads: a rotation of
+  // buffers compiles to register moves at the loop head and a conditional
+  // load to a branch, and either makes the loop wait for every load in
+  // flight instead of the one it needs.
   template <class F>
-  static __device__ __forceinline__ void walk(const Ctx& cx, int wave, int n_groups, F&& f) {
-    if (wave >= n_groups) return;
-    Keys cur = load(cx, wave * 32);
-    for (int gi = wave; gi < n_groups; gi += 4) {
-      Keys nxt;
-      if (gi + 4 < n_groups) nxt = load(cx, (gi + 4) * 32);
-      float z[16];
-      logits(cx, cur, gi * 32, z);
+  static __device__ __forceinline__ void walk(const Ctx& cx, int wave, int n_mg, F&& f) {
+    if (wave >= n_mg) return;
+    Keys ka = load(cx, wave * kMg);
+    Keys kb = load(cx, (wave + 4) * kMg);
+    int gi = wave;
+    for (; gi + 4 < n_mg; gi += 8) {
+      float z[kPr];
+      logits(cx, ka, gi * kMg, z);
       f(gi, z);
-      cur = nxt;
+      __builtin_amdgcn_sched_barrier(0);
+      ka = load(cx, (gi + 8) * kMg);
+      __builtin_amdgcn_sched_barrier(0);
+      float y[kPr];
+      logits(cx, kb, (gi + 4) * kMg, y);
+      f(gi + 4, y);
+      __builtin_amdgcn_sched_barrier(0);
+      kb = load(cx, (gi + 12) * kMg);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (gi < n_mg) {
+      float z[kPr];
+      logits(cx, ka, gi * kMg, z);
+      f(gi, z);
     }
   }
 };
 
-// row of register r of lane half hi
-__device__ __forceinline__ int reg_row(int r, int hi) { return 8 * ((r & 7) >> 2) + 4 * hi + (r & 3) + 16 * (r >> 3); }
+// x[l] + x[l ^ 16] + x[l ^ 32] + x[l ^ 48]: the sum over the four probe quads
+// of a tile's column (v_permlane16_swap, then v_permlane32_swap)
+__device__ __forceinline__ float quad_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void dyn_select_kernel(const DynLaunch a) {
   using S = Select<D>;
-  __shared__ float red[4][32][2];
-  __shared__ float red_max[4][2];
-  __shared__ int red_cnt[4][2];
+  extern __shared__ float score_lds[];  // [kQT][words * 32] when the scores fit
+  __shared__ float red_l[4][16 * kQT];
+  __shared__ float red_m[4][16 * kQT];
+  __shared__ float red_max[4][kQT];
+  __shared__ int red_cnt[4][kQT];
 
-  const int pairs = (a.nq + 1) / 2;
-  const int u = static_cast<int>(blockIdx.x % pairs);
-  const int64_t bh = blockIdx.x / pairs;
-  const int h = static_cast<int>(bh % a.heads_q), b = static_cast<int>(bh / a.heads_q);
-  const int g = h / (a.heads_q / a.heads_kv);
+  const int groups = (a.nq + kQT - 1) / kQT;
+  const int64_t n_bh = a.n_rows / a.nq;  // batch * heads_q
+  const int u = groups - 1 - static_cast<int>(blockIdx.x / n_bh);
+  // consecutive blocks cycle through the KV heads
+  const int64_t i_bh = blockIdx.x % n_bh;
+  const int G = a.heads_q / a.heads_kv;
+  const int g = static_cast<int>(i_bh % a.heads_kv);
+  const int64_t j_bh = i_bh / a.heads_kv;
+  const int b = static_cast<int>(j_bh / G);
+  const int h = g * G + static_cast<int>(j_bh % G);
   const int N = a.seqlen;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t0 = 2 * u;
-  const bool has_t1 = t0 + 1 < a.nq;
+  const int t0 = kQT * u;
 
   typename S::Ctx cx;
-  cx.l32 = lane & 31;
-  cx.hi = lane >> 5;
-  const int nc0 = (min(N, (t0 + 1) * kBq) - 1) / kBk + 1;
-  const int nc1 = has_t1 ? (min(N, (t0 + 2) * kBq) - 1) / kBk + 1 : 0;
-  cx.nc = max(nc0, nc1);
+  cx.col = lane & 15;
+  cx.quad = lane >> 4;
+  cx.t0 = t0;
+  cx.n = N;
+  cx.n_qt = min(kQT, a.nq - t0);
+  cx.nc = (min(N, (t0 + cx.n_qt) * kBq) - 1) / kBk + 1;
   cx.c = a.scale * kLog2e;
   cx.kbar = static_cast<const uint16_t*>(a.pooled) + (static_cast<int64_t>(b) * a.heads_kv + g) * a.nkt * D;
-  {
-    // A operand: lane l holds probe row l % 32, channels 16 s + 8 hi .. + 7
-    const int row = cx.l32;
-    const int qr = (t0 + (row >> 4)) * kBq + (row & 15) * kProbeStep;
-    const bool valid = (row < 16 || has_t1) && qr < N;
+  // A operand: lane l holds probe l % 16 of block rb, channels 32 s + 8 (l / 16) .. + 7
+#pragma unroll
+  for (int rb = 0; rb < kQT; ++rb) {
+    const int qr = (t0 + rb) * kBq + cx.col * kProbeStep;
+    const bool valid = rb < cx.n_qt && qr < N;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + b * a.q_stride[0] + h * a.q_stride[1] +
-                         static_cast<int64_t>(valid ? qr : 0) * a.q_stride[2] + cx.hi * 8;
+                         static_cast<int64_t>(valid ? qr : 0) * a.q_stride[2] + cx.quad * 8;
 #pragma unroll
     for (int s = 0; s < S::kSteps; ++s) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (valid) w = *reinterpret_cast<const u32x4*>(qp + s * 16);
-      cx.q[s] = __builtin_bit_cast(bf16x8, w);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int pr = reg_row(r, cx.hi);
-      const int rr = (t0 + (pr >> 4)) * kBq + (pr & 15) * kProbeStep;
-      cx.probe_row[r] = ((pr < 16 || has_t1) && rr < N) ? rr : INT32_MIN;
+      if (valid) w = *reinterpret_cast<const u32x4*>(qp + s * 32);
+      cx.q[rb][s] = __builtin_bit_cast(bf16x8, w);
     }
   }
-  const int n_groups = (cx.nc + 31) / 32;
+  const int n_mg = (cx.nc + kMg - 1) / kMg;
+  const bool lds_scores = a.words * 32 <= kLdsScoreTiles;
+  const int tiles_lds = a.words * 32;
 
-  // pass 1: per-probe max and sum of exp2(z - max) over the tiles it sees
-  float m[16], l[16];
+  // references: each probe's logit on tile 0, as -c ref
+  float nref[kPr];
+  {
+    float z0[kPr];
+    S::raw(cx, S::load_tile0(cx), z0);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    m[r] = -INFINITY;
-    l[r] = 0.0f;
+    for (int x = 0; x < kPr; ++x) nref[x] = -z0[x] * cx.c;
   }
-  S::walk(cx, wave, n_groups, [&](int, const float (&z)[16]) {
+
+  // pass 1: this lane's share of l_p, and the largest c z - c ref it met
+  float l[kPr];
+  float over = -INFINITY;
+  auto sum_pass = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (z[r] == -INFINITY) continue;
-      const float mn = fmaxf(m[r], z[r]);
-      l[r] = l[r] * __builtin_amdgcn_exp2f(m[r] - mn) + __builtin_amdgcn_exp2f(z[r] - mn);
-      m[r] = mn;
-    }
-  });
-  // combine over the 32 lanes of each half-wave (same probes, other tiles)
+    for (int x = 0; x < kPr; ++x) l[x] = 0.0f;
+    over = -INFINITY;
+    S::walk(cx, wave, n_mg, [&](int, const float (&z)[kPr]) {
 #pragma unroll
-  for (int off = 1; off < 32; off <<= 1) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float mo = __shfl_xor(m[r], off), lo = __shfl_xor(l[r], off);
-      const float mn = fmaxf(m[r], mo);
-      if (mn != -INFINITY) {
-        l[r] = l[r] * __builtin_amdgcn_exp2f(m[r] - mn) + lo * __builtin_amdgcn_exp2f(mo - mn);
-        m[r] = mn;
+      for (int x = 0; x < kPr; ++x) {
+        const float e = fmaf(z[x], cx.c, nref[x]);
+        over = fmaxf(over, e);
+        l[x] += __builtin_amdgcn_exp2f(e);
       }
-    }
-  }
-  if (cx.l32 == 0) {
+    });
+  };
+  sum_pass();
+  if (__syncthreads_or(over > kRefMargin)) {
+    // a logit far above its reference: take each probe's exact maximum as
+    // the reference instead, then sum again (every term <= 1)
+    float mx[kPr];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int pr = reg_row(r, cx.hi);
-      red[wave][pr][0] = m[r];
-      red[wave][pr][1] = l[r];
+    for (int x = 0; x < kPr; ++x) mx[x] = -INFINITY;
+    S::walk(cx, wave, n_mg, [&](int, const float (&z)[kPr]) {
+#pragma unroll
+      for (int x = 0; x < kPr; ++x) mx[x] = fmaxf(mx[x], z[x] * cx.c);
+    });
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+      for (int x = 0; x < kPr; ++x) mx[x] = fmaxf(mx[x], __shfl_xor(mx[x], off));
+    if (cx.col == 0) {
+#pragma unroll
+      for (int x = 0; x < kPr; ++x) red_m[wave][S::probe_of(cx, x)] = mx[x];
     }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < kPr; ++x) {
+      const int p = S::probe_of(cx, x);
+      const float m = fmaxf(fmaxf(red_m[0][p], red_m[1][p]), fmaxf(red_m[2][p], red_m[3][p]));
+      nref[x] = m == -INFINITY ? 0.0f : -m;  // m is already in units of c z
+    }
+    sum_pass();
+  }
+  // l_p over the 16 lanes of each probe quad (same probes, other tiles), then
+  // over the waves
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+    for (int x = 0; x < kPr; ++x) l[x] += __shfl_xor(l[x], off);
+  if (cx.col == 0) {
+#pragma unroll
+    for (int x = 0; x < kPr; ++x) red_l[wave][S::probe_of(cx, x)] = l[x];
   }
   __syncthreads();
-  float inv_l[16];
+  // the normalisation 1 / l_p joins the exponent: exp2(c z - c ref - log2 l);
+  // a probe that does not exist weighs nothing
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int pr = reg_row(r, cx.hi);
-    float mm = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) mm = fmaxf(mm, red[w][pr][0]);
-    float ll = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-      if (red[w][pr][0] != -INFINITY) ll += red[w][pr][1] * __builtin_amdgcn_exp2f(red[w][pr][0] - mm);
-    m[r] = mm;
-    inv_l[r] = ll > 0.0f ? 1.0f / ll : 0.0f;
+  for (int x = 0; x < kPr; ++x) {
+    const int p = S::probe_of(cx, x);
+    const float ll = (red_l[0][p] + red_l[1][p]) + (red_l[2][p] + red_l[3][p]);
+    nref[x] = (ll > 0.0f && S::probe_exists(cx, x)) ? nref[x] - __log2f(ll) : -INFINITY;
   }
 
-  // pass 2: the largest tile score of each query tile
-  float smax0 = 0.0f, smax1 = 0.0f;
-  S::walk(cx, wave, n_groups, [&](int, const float (&z)[16]) {
-    const float p0 = S::partial_score(z, m, inv_l, 0), p1 = S::partial_score(z, m, inv_l, 8);
-    smax0 = fmaxf(smax0, p0 + __shfl_xor(p0, 32));
-    smax1 = fmaxf(smax1, p1 + __shfl_xor(p1, 32));
+  // score of this lane's tile for query tile t0 + rb, in every lane of the
+  // tile's column
+  auto score_rb = [&](const float (&z)[kPr], int rb) __attribute__((always_inline)) -> float {
+    float p = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p += __builtin_amdgcn_exp2f(fmaf(z[4 * rb + r], cx.c, nref[4 * rb + r]));
+    return quad_sum(p);
+  };
+
+  // pass 2: scores (to LDS when they fit) and their maximum per query tile
+  float smax[kQT];
+#pragma unroll
+  for (int rb = 0; rb < kQT; ++rb) smax[rb] = 0.0f;
+  S::walk(cx, wave, n_mg, [&](int gi, const float (&z)[kPr]) {
+    const int kt = gi * kMg + cx.col;
+    float mine = 0.0f;
+#pragma unroll
+    for (int rb = 0; rb < kQT; ++rb) {
+      const float sc = score_rb(z, rb);
+      smax[rb] = fmaxf(smax[rb], sc);
+      mine = cx.quad == rb ? sc : mine;
+    }
+    // quad q of the column stores query tile t0 + q's score (kQT = 4 quads)
+    if (lds_scores) score_lds[cx.quad * tiles_lds + kt] = mine;
   });
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    smax0 = fmaxf(smax0, __shfl_xor(smax0, off));
-    smax1 = fmaxf(smax1, __shfl_xor(smax1, off));
-  }
+  for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+    for (int rb = 0; rb < kQT; ++rb) smax[rb] = fmaxf(smax[rb], __shfl_xor(smax[rb], off));
   if (lane == 0) {
-    red_max[wave][0] = smax0;
-    red_max[wave][1] = smax1;
+#pragma unroll
+    for (int rb = 0; rb < kQT; ++rb) red_max[wave][rb] = smax[rb];
   }
   __syncthreads();
-  smax0 = fmaxf(fmaxf(red_max[0][0], red_max[1][0]), fmaxf(red_max[2][0], red_max[3][0]));
-  smax1 = fmaxf(fmaxf(red_max[0][1], red_max[1][1]), fmaxf(red_max[2][1], red_max[3][1]));
-  const float thr0 = a.alpha * smax0, thr1 = a.alpha * smax1;
 
-  // pass 3: keep bits, one word per 32-tile group and query tile
+  // keep bits, one 32-bit word per 32 tiles, two query tiles per ballot:
+  // lanes 0..31 decide tile t0 + 2 j's tiles, lanes 32..63 t0 + 2 j + 1's
   const int64_t row0 = (static_cast<int64_t>(b) * a.heads_q + h) * a.nq + t0;
-  uint32_t* bits0 = a.bitmap + row0 * a.words;
-  uint32_t* bits1 = bits0 + a.words;
-  int count0 = 0, count1 = 0;
-  S::walk(cx, wave, n_groups, [&](int gi, const float (&z)[16]) {
-    const float p0 = S::partial_score(z, m, inv_l, 0), p1 = S::partial_score(z, m, inv_l, 8);
-    const float sc0 = p0 + __shfl_xor(p0, 32), sc1 = p1 + __shfl_xor(p1, 32);
-    const int kt = gi * 32 + cx.l32;
-    const bool keep0 = kt < nc0 && (sc0 >= thr0 || kt * kBk + kBk - 1 > t0 * kBq);
-    const bool keep1 = kt < nc1 && (sc1 >= thr1 || kt * kBk + kBk - 1 > (t0 + 1) * kBq);
-    const uint32_t w0 = static_cast<uint32_t>(__ballot(keep0 && cx.hi == 0));
-    const uint32_t w1 = static_cast<uint32_t>(__ballot(keep1 && cx.hi == 0));
-    if (lane == 0) {
-      if (gi * 32 < nc0) bits0[gi] = w0;
-      if (has_t1) bits1[gi] = w1;
+  const int hi = lane >> 5, l32 = lane & 31;
+  const int n_words = (cx.nc + 31) / 32;
+  int count[kQT];
+#pragma unroll
+  for (int rb = 0; rb < kQT; ++rb) count[rb] = 0;
+  if (lds_scores) __syncthreads();  // every score written
+#pragma unroll
+  for (int j = 0; j < kQT / 2; ++j) {
+    const int rb = 2 * j + hi;  // this lane's query tile of the pair
+    const int tq = t0 + rb;
+    const int nc_q = rb < cx.n_qt ? (min(N, (tq + 1) * kBq) - 1) / kBk + 1 : 0;
+    const float thr = a.alpha * fmaxf(fmaxf(red_max[0][rb], red_max[1][rb]), fmaxf(red_max[2][rb], red_max[3][rb]));
+    const int nc_lo = 2 * j < cx.n_qt ? (min(N, (t0 + 2 * j + 1) * kBq) - 1) / kBk + 1 : 0;
+    for (int wi = wave; wi < n_words; wi += 4) {
+      float sc;
+      if (lds_scores) {
+        sc = score_lds[rb * tiles_lds + wi * 32 + l32];
+      } else {
+        // recompute: mini-groups 2 wi and 2 wi + 1 of word wi; this lane's
+        // tile l32 lies in the one of parity l32 / 16
+        float s2[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int gi = 2 * wi + half;
+          float z[kPr];
+          S::logits(cx, S::load(cx, gi * kMg), gi * kMg, z);
+          float v = 0.0f;
+#pragma unroll
+          for (int q = 0; q < kQT; ++q) {
+            const float s_q = score_rb(z, q);
+            v = rb == q ? s_q : v;
+          }
+          s2[half] = v;
+        }
+        sc = (l32 >> 4) == 0 ? s2[0] : s2[1];
+      }
+      const int kt = wi * 32 + l32;
+      const bool keep = kt < nc_q && (sc >= thr || kt * kBk + kBk - 1 > tq * kBq);
+      const uint64_t m = __ballot(keep);
+      const uint32_t w0 = static_cast<uint32_t>(m), w1 = static_cast<uint32_t>(m >> 32);
+      if (lane == 0) {
+        if (wi * 32 < nc_lo) a.bitmap[(row0 + 2 * j) * a.words + wi] = w0;
+        if (2 * j + 1 < cx.n_qt) a.bitmap[(row0 + 2 * j + 1) * a.words + wi] = w1;
+      }
+      count[2 * j] += __builtin_popcount(w0);
+      count[2 * j + 1] += __builtin_popcount(w1);
     }
-    count0 += __builtin_popcount(w0);
-    count1 += __builtin_popcount(w1);
-  });
+  }
   if (lane == 0) {
-    red_cnt[wave][0] = count0;
-    red_cnt[wave][1] = count1;
+#pragma unroll
+    for (int rb = 0; rb < kQT; ++rb) red_cnt[wave][rb] = count[rb];
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    a.counts[row0] = red_cnt[0][0] + red_cnt[1][0] + red_cnt[2][0] + red_cnt[3][0];
-    if (has_t1) a.counts[row0 + 1] = red_cnt[0][1] + red_cnt[1][1] + red_cnt[2][1] + red_cnt[3][1];
+  if (threadIdx.x < kQT && static_cast<int>(threadIdx.x) < cx.n_qt) {
+    const int rb = threadIdx.x;
+    a.counts[row0 + rb] = red_cnt[0][rb] + red_cnt[1][rb] + red_cnt[2][rb] + red_cnt[3][rb];
   }
 }
 
@@ -346,36 +483,28 @@ __global__ __launch_bounds__(1024) void dyn_scan_kernel(const DynLaunch a) {
 }
 
 // ---------------------------------------------------------------- emit
-// One wave per row: bitmap words -> ascending key tiles with causal flags.
+// One wave per row, 64 key tiles per step: lane l decides tile c0 + l from
+// the row's keep bits, and the kept tiles of the step go to consecutive list
+// positions (each lane's rank among the kept lanes below it).
 __global__ __launch_bounds__(256) void dyn_emit_kernel(const DynLaunch a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wave;
   if (row >= a.n_rows) return;
   const int t = static_cast<int>(row % a.nq);
   const int nc = (min(a.seqlen, (t + 1) * kBq) - 1) / kBk + 1;
-  const int n_words = (nc + 31) / 32;
   const uint32_t* bits = a.bitmap + row * a.words;
+  const uint64_t below = (uint64_t(1) << lane) - 1;
   int out = a.row_ptr[row];
-  for (int w0 = 0; w0 < n_words; w0 += 64) {
-    const int wi = w0 + lane;
-    uint32_t word = wi < n_words ? bits[wi] : 0u;
-    const int c = __builtin_popcount(word);
-    int incl = c;  // inclusive scan of the popcounts over the wave
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int v = __shfl_up(incl, off);
-      if (lane >= off) incl += v;
-    }
-    int pos = out + incl - c;
-    while (word) {
-      const int bit = __builtin_ctz(word);
-      word &= word - 1;
-      const int kt = wi * 32 + bit;
+  for (int c0 = 0; c0 < nc; c0 += 64) {
+    const int kt = c0 + lane;
+    const bool keep = kt < nc && ((bits[kt >> 5] >> (kt & 31)) & 1u);
+    const uint64_t m = __ballot(keep);
+    if (keep) {
+      const int pos = out + __popcll(m & below);
       a.k_tile[pos] = kt;
       a.flags[pos] = kt * kBk + kBk - 1 > t * kBq ? TRI_TILE_PARTIAL : TRI_TILE_FULL;
-      ++pos;
     }
-    out += __shfl(incl, 63);
+    out += __popcll(m);
   }
 }
 
@@ -383,8 +512,11 @@ template <int D>
 int launch_d(const DynLaunch& a, hipStream_t stream) {
   const int64_t pool_blocks = (a.n_pool_tiles + 3) / 4;
   hipLaunchKernelGGL(dyn_pool_kernel<D>, dim3(static_cast<unsigned>(pool_blocks)), dim3(256), 0, stream, a);
-  const int64_t select_blocks = a.n_rows / a.nq * ((a.nq + 1) / 2);
-  hipLaunchKernelGGL(dyn_select_kernel<D>, dim3(static_cast<unsigned>(select_blocks)), dim3(256), 0, stream, a);
+  const int64_t select_blocks = a.n_rows / a.nq * ((a.nq + kQT - 1) / kQT);
+  // LDS for the scores of the query tiles of a group, when they fit
+  const size_t score_bytes = a.words * 32 <= kLdsScoreTiles ? kQT * sizeof(float) * a.words * 32 : 0;
+  hipLaunchKernelGGL(dyn_select_kernel<D>, dim3(static_cast<unsigned>(select_blocks)), dim3(256), score_bytes,
+                     stream, a);
   hipLaunchKernelGGL(dyn_scan_kernel, dim3(1), dim3(1024), 0, stream, a);
   hipLaunchKernelGGL(dyn_emit_kernel, dim3(static_cast<unsigned>((a.n_rows + 3) / 4)), dim3(256), 0, stream,
                      a);
