@@ -537,21 +537,29 @@ struct Kernel {
     // softmax work instead of holding the MFMA-ready wave back.
     __builtin_amdgcn_s_setprio(1);
     const char LDS_AS* vp = stage + C::kKBytes + ln.v_rd;
+    constexpr int kPv = 2 * C::kOBlocks;
+    u32x4 vop[kPv];
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
+    for (int i = 0; i < kPv; ++i) {
+      const int kc = i / C::kOBlocks, ob = i % C::kOBlocks;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (LDS_AS i16x4*)(vp + ob * 64 + (kc * 16) * C::kVStride));
+      const i16x4 hv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (LDS_AS i16x4*)(vp + ob * 64 + (kc * 16 + 8) * C::kVStride));
+      const u32x2 w0 = __builtin_bit_cast(u32x2, lo);
+      const u32x2 w1 = __builtin_bit_cast(u32x2, hv);
+      vop[i] = u32x4{w0[0], w0[1], w1[0], w1[1]};
+    }
 #pragma unroll
-      for (int ob = 0; ob < C::kOBlocks; ++ob) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_AS i16x4*)(vp + ob * 64 + (kc * 16) * C::kVStride));
-        const i16x4 hv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_AS i16x4*)(vp + ob * 64 + (kc * 16 + 8) * C::kVStride));
-        // concatenate as integers: element-wise bf16 inserts of the 16-bit lanes
-        // are mis-selected by this compiler (they duplicate lane 0)
-        const u32x2 w0 = __builtin_bit_cast(u32x2, lo);
-        const u32x2 w1 = __builtin_bit_cast(u32x2, hv);
-        const u32x4 w = {w0[0], w0[1], w1[0], w1[1]};
-        st.o[ob] = mfma32(__builtin_bit_cast(bf16x8, w), pb[kc], st.o[ob]);
-      }
+    for (int i = 0; i < kPv; ++i)
+      st.o[i % C::kOBlocks] = mfma32(__builtin_bit_cast(bf16x8, vop[i]), pb[i / C::kOBlocks], st.o[i % C::kOBlocks]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // operands of the first two MFMAs
+#pragma unroll
+    for (int i = 0; i < kPv - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the operand of the MFMA two ahead
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_s_setprio(0);
   }
 
