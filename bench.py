@@ -245,11 +245,12 @@ def sample_of(o, lse, rows):
 
 def error_vs_oracle(sample, ref):
     """Max and mean |dO|, max |dLSE| / max(1, |LSE|) of a sample against the
-    oracle rows."""
+    oracle rows, and mean |O| of the oracle rows (the scale of the errors)."""
     o, l = sample
     _, ro, rl = ref
     err = np.abs(o - ro)
     return {"o_max_abs_err": float(f"{err.max():.3e}"), "o_mean_abs_err": float(f"{err.mean():.3e}"),
+            "o_mean_abs_exact": float(f"{np.abs(ro).mean():.3e}"),
             "lse_max_rel_err": float(f"{(np.abs(l - rl) / np.maximum(1.0, np.abs(rl))).max():.3e}")}
 
 
