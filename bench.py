@@ -243,6 +243,33 @@ def sample_of(o, lse, rows):
             lse[:, :, idx].cpu().numpy().astype(np.float64))
 
 
+def full_oracle(bits, cfg, plan, tri, o, lse):
+    """The fp64 oracle on every row of the layer, timed on the host, and the
+    whole GPU layer (one more launch) against it."""
+    import torch
+    from oracle import attention as oatt
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    print("[bench] full-layer oracle ...", file=sys.stderr, flush=True)
+    f64 = synth.bf16_bits_to_f64
+    q, k, v = f64(bits[0]), f64(bits[1]), f64(bits[2])
+    t0 = time.perf_counter()
+    ro, rl = oatt.attention(q, k, v, "triangle", cfg["sink"], cfg["window"], cfg["last_q"])
+    dt = time.perf_counter() - t0
+    tri()
+    torch.cuda.synchronize()
+    err = error_vs_oracle((o.float().cpu().numpy(), lse.cpu().numpy()), (None, ro, rl))
+    flops = 4.0 * 128 * 64 * cfg["d"] * plan.k_tile.size * cfg["Hq"] * cfg["B"]
+    print(f"[bench] full-layer oracle: {dt:.1f} s on {threads} threads", file=sys.stderr, flush=True)
+    return {"seconds": round(dt, 2), "cores": int(threads), "rows": int(q.shape[1] * q.shape[2]),
+            "tflops": round(flops / dt / 1e12, 6), "gpu_layer_vs_oracle": err}
+
+
 def error_vs_oracle(sample, ref):
     """Max and mean |dO|, max |dLSE| / max(1, |LSE|) of a sample against the
     oracle rows, and mean |O| of the oracle rows (the scale of the errors)."""
@@ -394,6 +421,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the 2.5 s shader-clock run (profiling runs)")
+    ap.add_argument("--full-oracle", action="store_true",
+                    help="also time the fp64 oracle on every row of the layer (about a minute on 16 "
+                         "host cores at 128K) and compare the whole layer with it")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -497,6 +527,9 @@ def main(argv=None):
         extra["triangle_error_vs_oracle"] = error_vs_oracle(tri_sample, ref)
         for entry, sample in tier_samples:
             entry["error_vs_exact_triangle"] = error_vs_oracle(sample, ref)
+
+    if args.full_oracle:
+        extra["cpu_full_layer"] = full_oracle(bits, cfg, plan, tri, o, lse)
 
     traffic = read_traffic(args.config)
     out = {
