@@ -240,7 +240,7 @@ struct QuantLaunch {
   int64_t n_blocks;  // batch * heads_kv * ceil(N / 64): one scale per key tile
   int32_t fp4;       // 0: fp8 copy (d bytes per row), 1: fp4 copy (d / 2 bytes per row)
   void* k8;          // out: fp8 [B, Hkv, N, d bytes] or fp4 [B, Hkv, N, d / 2 bytes]
-  float* scale;      // out: [B, Hkv, ceil(N / 32)]
+  float* scale;      // out: [B, Hkv, ceil(N / 64)], one per key tile
 };
 
 // Enqueue the fp8 quantization of K; returns TRI_OK or TRI_ERR_HIP.
