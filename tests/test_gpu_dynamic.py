@@ -64,20 +64,21 @@ def check_row(got, flags, want, scores, t, N):
     return np.array_equal(got, want)
 
 
-CASES = [  # N, d, Hq, Hkv, alpha, qscale
-    (1000, 128, 4, 2, 0.5, 4.0),
-    (777, 64, 3, 1, 0.3, 8.0),
-    (1, 128, 2, 1, 0.5, 1.0),
-    (2500, 128, 2, 2, 0.9, 4.0),
-    (700, 128, 4, 1, 1.0, 6.0),
-    (129, 64, 2, 2, 0.2, 3.0),
+CASES = [  # N, d, B, Hq, Hkv, alpha, qscale
+    (1000, 128, 1, 4, 2, 0.5, 4.0),
+    (777, 64, 1, 3, 1, 0.3, 8.0),
+    (1, 128, 1, 2, 1, 0.5, 1.0),
+    (2500, 128, 1, 2, 2, 0.9, 4.0),
+    (700, 128, 1, 4, 1, 1.0, 6.0),
+    (129, 64, 1, 2, 2, 0.2, 3.0),
+    (900, 128, 2, 4, 2, 0.6, 5.0),   # batch 2: rows (b * Hq + h) * nq + t
+    (600, 128, 2, 7, 1, 0.5, 4.0),   # seven query heads per KV head (the Qwen2.5-7B grouping)
 ]
 
 
-@pytest.mark.parametrize("N,d,Hq,Hkv,alpha,qscale", CASES)
-def test_pooled_keys_lists_and_attention(dev, N, d, Hq, Hkv, alpha, qscale):
-    gu.note(f"dynamic N={N} d={d} Hq={Hq} Hkv={Hkv} alpha={alpha} qscale={qscale}")
-    B = 1
+@pytest.mark.parametrize("N,d,B,Hq,Hkv,alpha,qscale", CASES)
+def test_pooled_keys_lists_and_attention(dev, N, d, B, Hq, Hkv, alpha, qscale):
+    gu.note(f"dynamic N={N} d={d} B={B} Hq={Hq} Hkv={Hkv} alpha={alpha} qscale={qscale}")
     bits, (q, k, v) = peaky_inputs(100 + N, B, Hq, Hkv, N, d, qscale, dev)
     qf, kf, vf = (gu.as_f64(x) for x in bits)
     p, rp, kt, fl = gpu_plan(q, k, alpha)
@@ -111,14 +112,15 @@ def test_pooled_keys_lists_and_attention(dev, N, d, Hq, Hkv, alpha, qscale):
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
     ref = odyn.attention_tiles(qf, kf, vf, rrp, rkt)
     own = odyn.attention_tiles(qf, kf, vf, rp, kt)
-    for h in range(Hq):
-        ro, rl = ref[(0, h)]
-        go, gl = own[(0, h)]
-        for t in range(nq):
-            rows = slice(t * 128, min(N, (t + 1) * 128))
-            gu.check(o[0, h, rows], lse[0, h, rows], go[rows], gl[rows], f"h={h} t={t} (GPU list)")
-            if same[h * nq + t]:
-                gu.check(o[0, h, rows], lse[0, h, rows], ro[rows], rl[rows], f"h={h} t={t}")
+    for b in range(B):
+        for h in range(Hq):
+            ro, rl = ref[(b, h)]
+            go, gl = own[(b, h)]
+            for t in range(nq):
+                rows = slice(t * 128, min(N, (t + 1) * 128))
+                gu.check(o[b, h, rows], lse[b, h, rows], go[rows], gl[rows], f"b={b} h={h} t={t} (GPU list)")
+                if same[(b * Hq + h) * nq + t]:
+                    gu.check(o[b, h, rows], lse[b, h, rows], ro[rows], rl[rows], f"b={b} h={h} t={t}")
 
 
 def test_alpha_zero_lists_are_causal_and_bit_identical_to_dense(dev):

@@ -217,6 +217,28 @@ def test_three_tier_layer_matches_the_oracle(dev, N, d, Hq, Hkv, sink, window, l
     gu.note(f"  max|dO|={err:.2e} max rel dLSE={rel:.2e}")
 
 
+def test_three_tiers_batch_two_and_seven_heads_per_kv_head(dev):
+    # batch 2 (the K copies and scales are per (batch, KV head)) and the
+    # Qwen2.5-7B grouping of seven query heads per KV head, each head with its
+    # own pair of boundaries
+    N, d, B, Hq, Hkv = 600, 128, 2, 7, 1
+    dist8 = [0, 64, 10 ** 6, -63, 128, 0, 256]
+    dist4 = [256, 10 ** 6, 0, 192, 10 ** 6, 64, 320]
+    gu.note(f"three tiers N={N} B={B} Hq={Hq} Hkv={Hkv}")
+    bits, (q, k, v) = gu.make_inputs(95, B, Hq, Hkv, N, d, dev)
+    qk = tsa.quantize_k(q, k, fp4=True)
+    o = torch.full((B, Hq, N, d), float("nan"), dtype=torch.float32, device=dev)
+    lse = torch.full((B, Hq, N), float("nan"), dtype=torch.float32, device=dev)
+    kw = dict(sink=64, window=200, last_q=100)
+    tsa.prefill(q, k, v, mode="tiered", plan=qk, low_dist=dist8, fp4_dist=dist4, o_dtype=torch.float32,
+                out=o, lse=lse, **kw)
+    torch.cuda.synchronize()
+    qf, kf, vf = (gu.as_f64(x) for x in bits)
+    ro, rl = otiers.attention(qf, kf, vf, kw["sink"], kw["window"], kw["last_q"], dist8, dist4=dist4)
+    err, rel = gu.check(o, lse, ro, rl, "three tiers B=2 G=7")
+    gu.note(f"  max|dO|={err:.2e} max rel dLSE={rel:.2e}")
+
+
 def test_unreached_fp4_boundary_is_bit_identical_to_two_tiers(dev):
     gu.note("fp4 boundary past N vs the two-tier layer, N=1500")
     N = 1500
