@@ -242,9 +242,13 @@ def test_dyn_plan_noalloc_rejects_bad_arguments():
     assert wsb > tsa.TRI_DYN_SCRATCH_BYTES
     assert call(tt=big, cap=nnzb) == tsa.TRI_ERR_CAPACITY
     assert "scratch" in tsa.last_error()
-    # the largest Llama-shaped layer it holds: N = 262144
-    edge = _good_tensors(N=1 << 18, Hq=32, Hkv=8)
+    # the largest Llama-shaped layer (batch 1) it holds is N = 337920: the next
+    # query tile (N + 128) needs more than the array
+    edge = _good_tensors(N=337920, Hq=32, Hkv=8)
     assert tsa.tri_dyn_plan_sizes(edge)[0] <= tsa.TRI_DYN_SCRATCH_BYTES
+    past = _good_tensors(N=337920 + 128, Hq=32, Hkv=8)
+    assert tsa.tri_dyn_plan_sizes(past)[0] > tsa.TRI_DYN_SCRATCH_BYTES
+    assert call(tt=past, cap=tsa.tri_dyn_plan_sizes(past)[2]) == tsa.TRI_ERR_CAPACITY
     z = _good_tensors(N=0)
     assert call(tt=z, cap=tsa.tri_dyn_plan_sizes(z)[2]) == tsa.TRI_OK
 
