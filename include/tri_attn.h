@@ -223,7 +223,7 @@ int tri_dyn_plan(const tri_attn_tensors* t, const tri_dyn_params* dp, void* d_wo
  * device is used (`stream` must belong to it).  A layer whose workspace
  * (tri_dyn_plan_sizes) exceeds TRI_DYN_SCRATCH_BYTES is rejected with
  * TRI_ERR_CAPACITY before any HIP call (64 MiB covers e.g. 32 query / 8 KV
- * heads, d = 128, up to N = 262144 at batch 1).  Every call on one GPU
+ * heads, d = 128, up to N = 337920 at batch 1).  Every call on one GPU
  * shares that GPU's array and leaves its contents behind (nothing in it
  * needs to start at zero): calls that overlap on one GPU -- on two streams,
  * or from two threads -- race and must be serialised by the caller.
